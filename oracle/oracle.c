@@ -1,0 +1,539 @@
+/*
+ * oracle.c -- plain, slow, CPU oracle for the group-quantized matmul and the
+ * routed mixture-of-experts FFN.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU
+ * baseline leg of the benchmark load this library.  It shares no code, header,
+ * table or constant with the GPU library, and it never reads anything that the
+ * GPU library wrote.
+ *
+ * Build: C99 + OpenMP, -O2 -ffp-contract=off, never -ffast-math (fast-math
+ * would turn the fp32 divisions of the quantizer into reciprocal multiplies and
+ * change quantized codes).
+ *
+ * Sources (cited by page title and section):
+ *   [P1] "Hand-writing a DeepSeek inference engine in pure C"
+ *        (hnwysp.cn/news/134870):
+ *        §2.3  group-wise asymmetric quantization, group 64 or 128, dequant
+ *              formula (q - zero_point) * scale;
+ *        §3.2  the quantize_group routine (per-group min/max,
+ *              scale = (max - min) / (2^bits - 1), zp = round(-min / scale),
+ *              q = clamp(round(v / scale) + zp)); INT4 = two values per byte,
+ *              same rule over 0..15; dequant fused into the matmul inner loop;
+ *        §3.3  the matmul C = A * B (reduction over K);
+ *        §3.4  softmax with the maximum subtracted first;
+ *        §3.5  MoE router = linear layer + softmax + top-k (partial sort of
+ *              (score, index) pairs, greater-first), tokens grouped per expert,
+ *              weighted sum of the expert outputs;
+ *        §5.1/§5.3  a zero scale is an error (assert scale != 0).
+ *   [P3] "Running a 284B-parameter LLM from 3.2 GB of RAM in plain C"
+ *        (feinterview.poetries.top): the scalar and OpenMP CPU paths must be
+ *        bitwise identical (fixed accumulator tree, no fp contraction).
+ *
+ * Readings where the pages are silent or garbled are listed in the design doc and
+ * restated next to the code that takes them.
+ */
+#include <float.h>
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_FLAG_DEGENERATE 1u /* scale == 0 / not finite, or |zp| > 2^24 */
+#define ORC_FLAG_NONFINITE 2u  /* a NaN or infinity among the group's inputs */
+
+void orc_set_threads(int32_t n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
+int32_t orc_max_threads(void) {
+#ifdef _OPENMP
+  return (int32_t)omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* Canonical quantized format (the oracle's own):                            */
+/*   q     : INT8 -> one byte per weight, row-major [rows][K], value 0..255   */
+/*           INT4 -> [rows][K/2]; byte j of a row holds k = 2j in its low    */
+/*           nibble and k = 2j+1 in its high nibble                          */
+/*   scale : fp32 [rows][K/group]                                            */
+/*   zp    : fp32 [rows][K/group], an exact integer                          */
+/* [P1] §3.2 stores int8(q - 128); the byte used here is that byte XOR 0x80. */
+/* ------------------------------------------------------------------------ */
+
+static int32_t orc_get_q(const uint8_t* q, int64_t K, int32_t bits, int64_t r, int64_t k) {
+  if (bits == 8) return (int32_t)q[r * K + k];
+  uint8_t byte = q[r * (K / 2) + k / 2];
+  return (k & 1) ? (int32_t)(byte >> 4) : (int32_t)(byte & 0x0F);
+}
+
+/*
+ * [P1] §3.2 quantize_group, applied to every group of `group` consecutive
+ * elements along K of every row.  All arithmetic is IEEE fp32, as in the
+ * printed routine: scale = (max - min) / 255.0f (or / 15.0f for INT4),
+ * zp = (int32) roundf(-min / scale), q = clamp((int32) roundf(v / scale) + zp,
+ * 0, 2^bits - 1).  roundf rounds half-way cases away from zero.
+ *
+ * Flagged groups ([P1] §5.1: a zero scale must not be used) get q = 0,
+ * scale = 0, zp = 0 and a nonzero gflags entry.  Returns the number of flagged
+ * groups, or -1 for invalid arguments.
+ */
+int64_t orc_quantize(const float* w, int64_t rows, int64_t K, int32_t bits, int32_t group,
+                     uint8_t* q, float* scale, float* zp, uint8_t* gflags) {
+  if (!w || !q || !scale || !zp || rows < 0 || K <= 0) return -1;
+  if (bits != 8 && bits != 4) return -1;
+  if (group <= 0 || K % group != 0) return -1;
+  if (bits == 4 && (K % 2) != 0) return -1;
+  const int32_t qmax = (1 << bits) - 1;
+  const float levels = (float)qmax; /* 255.0f or 15.0f */
+  const int64_t ngroups = K / group;
+  const int64_t row_bytes = (bits == 8) ? K : K / 2;
+  int64_t nflag = 0;
+
+#pragma omp parallel for schedule(static) reduction(+ : nflag)
+  for (int64_t r = 0; r < rows; ++r) {
+    memset(q + r * row_bytes, 0, (size_t)row_bytes);
+    for (int64_t g = 0; g < ngroups; ++g) {
+      const float* src = w + r * K + g * group;
+      uint8_t flag = 0;
+      float lo = FLT_MAX, hi = -FLT_MAX;
+      for (int32_t i = 0; i < group; ++i) {
+        float v = src[i];
+        if (!isfinite(v)) flag |= ORC_FLAG_NONFINITE;
+        if (v < lo) lo = v;
+        if (v > hi) hi = v;
+      }
+      float s = 0.0f;
+      float zr = 0.0f;
+      if (!flag) {
+        s = (hi - lo) / levels;
+        if (!(s > 0.0f) || !isfinite(s)) {
+          flag |= ORC_FLAG_DEGENERATE;
+        } else {
+          zr = roundf(-lo / s);
+          /* zp is kept as an fp32 holding an exact integer; beyond 2^24 it
+             would not be exact (and beyond 2^31 the int32 cast of the printed
+             routine is undefined), so such groups are flagged instead. */
+          if (!(fabsf(zr) <= 16777216.0f)) flag |= ORC_FLAG_DEGENERATE;
+        }
+      }
+      const int64_t gi = r * ngroups + g;
+      if (gflags) gflags[gi] = flag;
+      if (flag) {
+        scale[gi] = 0.0f;
+        zp[gi] = 0.0f;
+        ++nflag;
+        continue;
+      }
+      const int32_t z = (int32_t)zr;
+      scale[gi] = s;
+      zp[gi] = (float)z;
+      for (int32_t i = 0; i < group; ++i) {
+        float v = src[i];
+        int32_t qi = (int32_t)roundf(v / s) + z;
+        if (qi < 0) qi = 0;
+        if (qi > qmax) qi = qmax;
+        const int64_t k = g * group + i;
+        if (bits == 8) {
+          q[r * row_bytes + k] = (uint8_t)qi;
+        } else {
+          uint8_t* b = q + r * row_bytes + k / 2;
+          if (k & 1) *b = (uint8_t)((*b & 0x0F) | (qi << 4));
+          else       *b = (uint8_t)((*b & 0xF0) | qi);
+        }
+      }
+    }
+  }
+  return nflag;
+}
+
+/* [P1] §2.3: w = (q - zero_point) * scale.  In fp64 this is exact: q - zp is
+   an integer below 2^25 in magnitude and scale has a 24-bit significand. */
+void orc_dequant_f64(const uint8_t* q, const float* scale, const float* zp, int64_t rows,
+                     int64_t K, int32_t bits, int32_t group, double* w) {
+  const int64_t ngroups = K / group;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t gi = r * ngroups + k / group;
+      w[r * K + k] = ((double)orc_get_q(q, K, bits, r, k) - (double)zp[gi]) * (double)scale[gi];
+    }
+}
+
+/* The same formula in fp32: (float)(q - zp) is exact, so one rounding. */
+void orc_dequant_f32(const uint8_t* q, const float* scale, const float* zp, int64_t rows,
+                     int64_t K, int32_t bits, int32_t group, float* w) {
+  const int64_t ngroups = K / group;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t gi = r * ngroups + k / group;
+      w[r * K + k] = ((float)orc_get_q(q, K, bits, r, k) - zp[gi]) * scale[gi];
+    }
+}
+
+/*
+ * Plain reference matmul in fp64 ([P1] §3.3 semantics, with the weight stored
+ * as W[N][K] so the reduction runs along a row): Y[m][n] = sum_k X[m][k] *
+ * W[n][k], summed in k order.  S[m][n] = sum_k |X[m][k] * W[n][k]| is the
+ * magnitude sum that scales every floating-point tolerance.  Either output
+ * pointer may be NULL.
+ */
+void orc_matmul_f64(const double* X, int64_t M, const double* W, int64_t N, int64_t K, double* Y,
+                    double* S) {
+#pragma omp parallel for collapse(2) schedule(static)
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0, mag = 0.0;
+      for (int64_t k = 0; k < K; ++k) {
+        const double p = X[m * K + k] * W[n * K + k];
+        acc += p;
+        mag += fabs(p);
+      }
+      if (Y) Y[m * N + n] = acc;
+      if (S) S[m * N + n] = mag;
+    }
+}
+
+/*
+ * The pages' own CPU method in fp32 ([P1] §3.2 "dequantize inside the inner
+ * loop while accumulating", §3.3 OpenMP over independent outputs):
+ *   Y[m][n] = sum_k X[m][k] * ((q[n][k] - zp) * scale)
+ * Each product is added into one of 16 partial sums (k mod 16); the partial
+ * sums are then added in a fixed pairwise tree.  Every output's arithmetic is
+ * the same whatever the thread count, so the 1-thread and the OpenMP runs are
+ * bitwise identical ([P3]).  Rows of X are indexed through `xrows` when it is
+ * not NULL (the expert-grouped batch of [P1] §3.5).
+ */
+static float orc_tree16(float* a) {
+  for (int w = 8; w >= 1; w >>= 1)
+    for (int i = 0; i < w; ++i) a[i] = a[i] + a[i + w];
+  return a[0];
+}
+
+static void orc_qdot_rows_f32(const float* X, const int64_t* xrows, int64_t M, const uint8_t* q,
+                              const float* scale, const float* zp, int64_t n, int64_t K,
+                              int32_t bits, int32_t group, float* out, int64_t out_stride) {
+  const int64_t ngroups = K / group;
+  for (int64_t m = 0; m < M; ++m) {
+    const float* x = X + (xrows ? xrows[m] : m) * K;
+    float part[16];
+    for (int i = 0; i < 16; ++i) part[i] = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+      const int64_t gi = n * ngroups + k / group;
+      const float wq = ((float)orc_get_q(q, K, bits, n, k) - zp[gi]) * scale[gi];
+      const float p = x[k] * wq;
+      part[k & 15] = part[k & 15] + p;
+    }
+    out[m * out_stride] = orc_tree16(part);
+  }
+}
+
+void orc_qmatmul_f32(const float* X, int64_t M, const uint8_t* q, const float* scale,
+                     const float* zp, int64_t N, int64_t K, int32_t bits, int32_t group,
+                     float* Y) {
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n)
+    orc_qdot_rows_f32(X, NULL, M, q, scale, zp, n, K, bits, group, Y + n, N);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Router and routing ([P1] §3.4, §3.5)                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Router = linear layer ([P1] §3.5): l[t][e] = sum_h X[t][h] * Wr[e][h]
+   (+ bias[e] when bias is not NULL), in fp64.  S = magnitude sums. */
+void orc_router_f64(const double* X, int64_t T, const double* Wr, const double* bias, int32_t E,
+                    int64_t H, double* logits, double* S) {
+  orc_matmul_f64(X, T, Wr, E, H, logits, S);
+  if (bias)
+    for (int64_t t = 0; t < T; ++t)
+      for (int32_t e = 0; e < E; ++e) logits[t * E + e] += bias[e];
+}
+
+/* "a ranks before b": larger logit first; equal logits -> larger index first,
+   which is what a greater-than partial sort over (score, index) pairs gives
+   ([P1] §3.5; the comparison characters were lost in extraction). */
+static int orc_before(double la, int32_t ia, double lb, int32_t ib) {
+  if (la != lb) return la > lb;
+  return ia > ib;
+}
+
+/*
+ * Softmax + top-k + renormalisation for each token.
+ *   p_e = exp(l_e - max) / sum_j exp(l_j - max)      ([P1] §3.4: subtract max)
+ *   idx = the k experts ranked first by orc_before, in that order ([P1] §3.5)
+ *   w_i = p_{idx_i} / sum_j p_{idx_j}                 (weights sum to one)
+ * Selection uses the logits themselves, as the printed route() does, so two
+ * distinct logits are never merged by rounding in exp.  gap[t] (nullable) is
+ * the logit distance between the k-th and the (k+1)-th ranked experts
+ * (+inf when k == E); tests use it to tell near-ties apart.
+ * Logits must be finite; returns -1 otherwise or for invalid arguments.
+ */
+int32_t orc_route(const double* logits, int64_t T, int32_t E, int32_t k, int32_t* idx, double* w,
+                  double* gap) {
+  if (E <= 0 || k <= 0 || k > E) return -1;
+  for (int64_t i = 0; i < T * E; ++i)
+    if (!isfinite(logits[i])) return -1;
+  unsigned char* taken = (unsigned char*)malloc((size_t)E);
+  double* p = (double*)malloc(sizeof(double) * (size_t)E);
+  if (!taken || !p) {
+    free(taken);
+    free(p);
+    return -1;
+  }
+  for (int64_t t = 0; t < T; ++t) {
+    const double* l = logits + t * E;
+    double mx = l[0];
+    for (int32_t e = 1; e < E; ++e)
+      if (l[e] > mx) mx = l[e];
+    double z = 0.0;
+    for (int32_t e = 0; e < E; ++e) {
+      p[e] = exp(l[e] - mx);
+      z += p[e];
+    }
+    for (int32_t e = 0; e < E; ++e) p[e] /= z;
+    memset(taken, 0, (size_t)E);
+    double sel = 0.0;
+    for (int32_t i = 0; i < k; ++i) {
+      int32_t best = -1;
+      for (int32_t e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        if (best < 0 || orc_before(l[e], e, l[best], best)) best = e;
+      }
+      taken[best] = 1;
+      idx[t * k + i] = best;
+      sel += p[best];
+    }
+    for (int32_t i = 0; i < k; ++i) w[t * k + i] = p[idx[t * k + i]] / sel;
+    if (gap) {
+      if (k == E) {
+        gap[t] = INFINITY;
+      } else {
+        int32_t next = -1;
+        for (int32_t e = 0; e < E; ++e) {
+          if (taken[e]) continue;
+          if (next < 0 || orc_before(l[e], e, l[next], next)) next = e;
+        }
+        gap[t] = l[idx[t * k + k - 1]] - l[next];
+      }
+    }
+  }
+  free(taken);
+  free(p);
+  return 0;
+}
+
+/*
+ * Group the T*k routing entries by expert ([P1] §3.5: gather the tokens routed
+ * to one expert so its weights are read once).  A stable counting sort:
+ *   counts[e]  = number of entries j = t*k+i with idx[j] == e
+ *   offsets[e] = sum of counts below e (offsets[E] = T*k)
+ *   perm       = every entry j, ordered by (expert, j)
+ */
+int32_t orc_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, int32_t* counts,
+                  int32_t* offsets, int32_t* perm) {
+  const int64_t n = T * k;
+  for (int32_t e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t j = 0; j < n; ++j) {
+    if (idx[j] < 0 || idx[j] >= E) return -1;
+    counts[idx[j]]++;
+  }
+  offsets[0] = 0;
+  for (int32_t e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int32_t* fill = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+  if (!fill) return -1;
+  for (int32_t e = 0; e < E; ++e) fill[e] = offsets[e];
+  for (int64_t j = 0; j < n; ++j) perm[fill[idx[j]]++] = (int32_t)j;
+  free(fill);
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* One expert: SwiGLU FFN over group-quantized weights                       */
+/* ------------------------------------------------------------------------ */
+
+static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* d/dz silu(z) = s(z) * (1 + z * (1 - s(z))), s = logistic */
+static double orc_dsilu(double z) {
+  const double s = 1.0 / (1.0 + exp(-z));
+  return s * (1.0 + z * (1.0 - s));
+}
+
+typedef struct {
+  const uint8_t* q;
+  const float* scale;
+  const float* zp;
+} orc_qmat;
+
+/* dot of x (fp64, length K) with the exact fp64 dequantized row n */
+static void orc_qrow_dot_f64(const double* x, orc_qmat W, int64_t n, int64_t K, int32_t bits,
+                             int32_t group, double* dot, double* mag) {
+  const int64_t ngroups = K / group;
+  double acc = 0.0, s = 0.0;
+  for (int64_t k = 0; k < K; ++k) {
+    const int64_t gi = n * ngroups + k / group;
+    const double wv =
+        ((double)orc_get_q(W.q, K, bits, n, k) - (double)W.zp[gi]) * (double)W.scale[gi];
+    const double p = x[k] * wv;
+    acc += p;
+    s += fabs(p);
+  }
+  *dot = acc;
+  *mag = s;
+}
+
+/*
+ * One expert in fp64:  g = x Wg^T, u = x Wu^T (I outputs, K = H),
+ * h = silu(g) * u, y = h Wd^T (H outputs, K = I); silu(z) = z / (1 + e^-z).
+ * Expert FFN form: SwiGLU, as the workload defines (the pages only call the
+ * experts feed-forward networks).
+ * Tolerance helpers (all nullable):
+ *   Sd[n]  = sum_j |h_j * Wd[n][j]|
+ *   Pd[n]  = sum_j dh_j * |Wd[n][j]| with
+ *            dh_j = |silu'(g_j) u_j| * Sg_j + |silu(g_j)| * Su_j,
+ *            Sg_j, Su_j the magnitude sums of g_j and u_j: the first-order
+ *            effect on y of a relative error of 1 in the gate/up sums.
+ *   g, u, h (length I) are returned when their pointers are not NULL.
+ */
+void orc_expert_f64(const double* x, int64_t H, int64_t I, const uint8_t* gq, const float* gs,
+                    const float* gz, const uint8_t* uq, const float* us, const float* uz,
+                    const uint8_t* dq, const float* ds, const float* dz, int32_t bits,
+                    int32_t group, double* y, double* Sd, double* Pd, double* g_out,
+                    double* u_out, double* h_out) {
+  orc_qmat Wg = {gq, gs, gz}, Wu = {uq, us, uz}, Wd = {dq, ds, dz};
+  double* h = (double*)malloc(sizeof(double) * (size_t)I);
+  double* dh = (double*)malloc(sizeof(double) * (size_t)I);
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < I; ++j) {
+    double g, sg, u, su;
+    orc_qrow_dot_f64(x, Wg, j, H, bits, group, &g, &sg);
+    orc_qrow_dot_f64(x, Wu, j, H, bits, group, &u, &su);
+    h[j] = orc_silu(g) * u;
+    dh[j] = fabs(orc_dsilu(g) * u) * sg + fabs(orc_silu(g)) * su;
+    if (g_out) g_out[j] = g;
+    if (u_out) u_out[j] = u;
+    if (h_out) h_out[j] = h[j];
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < H; ++n) {
+    double acc, mag;
+    orc_qrow_dot_f64(h, Wd, n, I, bits, group, &acc, &mag);
+    y[n] = acc;
+    if (Sd) Sd[n] = mag;
+    if (Pd) {
+      const int64_t ngroups = I / group;
+      double pm = 0.0;
+      for (int64_t j = 0; j < I; ++j) {
+        const int64_t gi = n * ngroups + j / group;
+        const double wv =
+            ((double)orc_get_q(Wd.q, I, bits, n, j) - (double)Wd.zp[gi]) * (double)Wd.scale[gi];
+        pm += dh[j] * fabs(wv);
+      }
+      Pd[n] = pm;
+    }
+  }
+  free(h);
+  free(dh);
+}
+
+/* ------------------------------------------------------------------------ */
+/* The pages' CPU MoE in fp32 (timed as the CPU baseline)                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Token-routed MoE FFN, fp32, fused dequant (the same dot routine as
+ * orc_qmatmul_f32).  Experts are passed as pointer arrays indexed by expert id
+ * (entries of experts nobody selected may be NULL).  Routing (idx, w) is an
+ * input.  Y[t] = sum_i w[t][i] * y_{idx[t][i]}(X[t]), summed in slot order.
+ *
+ * grouped = 0: loop over tokens, then over the token's k experts.
+ * grouped = 1: group the entries by expert first ([P1] §3.5) and run each
+ *              expert once over its batch of tokens.  Both orders perform the
+ *              identical per-output arithmetic, so the outputs are bitwise
+ *              equal (a test checks this).
+ * h_ws must hold T*k*I floats, y_ws T*k*H floats.
+ */
+int32_t orc_moe_f32(const float* X, int64_t T, int64_t H, int64_t I, int32_t E, int32_t k,
+                    const int32_t* idx, const float* w, const uint8_t* const* gq,
+                    const float* const* gs, const float* const* gz, const uint8_t* const* uq,
+                    const float* const* us, const float* const* uz, const uint8_t* const* dq,
+                    const float* const* ds, const float* const* dz, int32_t bits, int32_t group,
+                    int32_t grouped, float* h_ws, float* y_ws, float* Y) {
+  const int64_t n = T * k;
+  int64_t* xrows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+  int64_t* hrows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n > 0 ? n : 1));
+  int32_t* counts = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
+  int32_t* offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
+  int32_t* perm = (int32_t*)malloc(sizeof(int32_t) * (size_t)(n > 0 ? n : 1));
+  if (!xrows || !hrows || !counts || !offsets || !perm) return -1;
+  if (orc_group(idx, T, k, E, counts, offsets, perm) != 0) return -1;
+
+  /* Build the batches: one per (token, slot) when token-looped, one per
+     expert when grouped.  h_ws / y_ws rows are indexed by entry j = t*k+i. */
+  const int64_t nb = grouped ? E : n;
+  for (int64_t b = 0; b < nb; ++b) {
+    int64_t cnt, e;
+    const int32_t* js;
+    int32_t one;
+    if (grouped) {
+      e = b;
+      cnt = counts[e];
+      js = perm + offsets[e];
+    } else {
+      one = (int32_t)b;
+      js = &one;
+      cnt = 1;
+      e = idx[b];
+    }
+    if (cnt == 0) continue;
+    for (int64_t m = 0; m < cnt; ++m) {
+      xrows[m] = js[m] / k;
+      hrows[m] = js[m];
+    }
+    /* gate and up: outputs j' in [0, I) for every token of the batch */
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < I; ++r) {
+      for (int64_t m = 0; m < cnt; ++m) {
+        float gv, uv;
+        orc_qdot_rows_f32(X, xrows + m, 1, gq[e], gs[e], gz[e], r, H, bits, group, &gv, 1);
+        orc_qdot_rows_f32(X, xrows + m, 1, uq[e], us[e], uz[e], r, H, bits, group, &uv, 1);
+        const float sg = gv / (1.0f + expf(-gv));
+        h_ws[hrows[m] * I + r] = sg * uv;
+      }
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < H; ++r) {
+      for (int64_t m = 0; m < cnt; ++m) {
+        float yv;
+        orc_qdot_rows_f32(h_ws, hrows + m, 1, dq[e], ds[e], dz[e], r, I, bits, group, &yv, 1);
+        y_ws[hrows[m] * H + r] = yv;
+      }
+    }
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t c = 0; c < H; ++c) {
+      float acc = 0.0f;
+      for (int32_t i = 0; i < k; ++i) acc = acc + w[t * k + i] * y_ws[(t * k + i) * H + c];
+      Y[t * H + c] = acc;
+    }
+  free(xrows);
+  free(hrows);
+  free(counts);
+  free(offsets);
+  free(perm);
+  return 0;
+}
