@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Benchmark of the group-quantized fused-dequant path on one MI355X.
+
+Headline step (the workload the metric is quoted on): one fp32 activation
+vector through a dense INT4 group-64 4096x4096 projection and an INT8
+group-64 vocab projection 4096x129280 (dsq_gemv twice).  `value` is the
+effective weight bandwidth of the step: canonical bytes moved (codes + fp32
+scale + fp32 zero point + activations + outputs) / wall time per step, with
+every input resident in HBM when timing starts.  The step streams ~607 MB,
+more than the 256 MB Infinity Cache, so no input stays cached across steps.
+
+`roofline` is for the dominant kernel (the vocab GEMV), timed per launch with
+HIP events on the stream it runs on.  `secondary` reports the other workloads
+(INT8 GEMV, MoE decode, batched MoE decode, dense and MoE prefill) with
+their own timings; `cpu_baseline` times the CPU oracle (the pages' own
+OpenMP fused-dequant loop) on a bounded sample of the headline workload.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def qbytes(bits, group, K, N):
+    """Canonical bytes of a quantized matrix: codes + fp32 (scale, zp)."""
+    return N * K * bits // 8 + N * (K // group) * 8
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "group_quantized_moe_dsq_amd", "csrc"))):
+        with open(os.path.join(ROOT, "group_quantized_moe_dsq_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record():
+    """HBM bytes per launch of the dominant kernel measured with rocprofv3
+    counters (profiles/traffic_vocab_gemv.json), if taken on this source."""
+    p = os.path.join(ROOT, "profiles", "traffic_vocab_gemv.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_calls(fn, iters, warmup, torch, graph=True, replays=5):
+    """Average ms per call.  With graph=True the `iters` calls are captured
+    once into a HIP graph and replayed, so host launch overhead does not hide
+    short kernels; HIP events on the replay stream bracket the replays."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(iters):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(replays):
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / (iters * replays)
+    s.record()
+    for i in range(iters):
+        fn(i)
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / iters  # ms
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path has no multi-GPU leg to run).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from group_quantized_moe_dsq_amd import dsq, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K = 4096
+    NV = 129280
+
+    # ---------------- headline workload ----------------
+    log("setup: INT4 g64 4096x4096 and INT8 g64 4096x129280")
+    w4 = synth.normal((4096, K), 0.02, 0, synth.W, 21, device=dev)
+    W4 = dsq.QWeight(4, 64, K, 4096)
+    dsq.pack_weights(w4, W4)
+    del w4
+    wv = synth.normal((NV, K), 0.02, 0, synth.W, 22, device=dev)
+    WV = dsq.QWeight(8, 64, K, NV)
+    dsq.pack_weights(wv, WV)
+    del wv
+    torch.cuda.empty_cache()
+    x = synth.normal((K,), 1.0, 0, synth.X, 21, device=dev)
+    y4 = torch.empty(4096, device=dev)
+    yv = torch.empty(NV, device=dev)
+    bytes4 = qbytes(4, 64, K, 4096) + K * 4 + 4096 * 4
+    bytesv = qbytes(8, 64, K, NV) + K * 4 + NV * 4
+    step_bytes = bytes4 + bytesv
+
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(i=None):
+        dsq.gemv(W4, x, y4)
+        if i is not None:
+            ev_s[i].record()
+        dsq.gemv(WV, x, yv)
+        if i is not None:
+            ev_e[i].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    vocab_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(ev_s, ev_e)]))
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = bytesv / (vocab_ms * 1e-3) / 1e9
+    log(f"headline: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s; vocab gemv "
+        f"{vocab_ms * 1e3:.1f} us = {achieved:.0f} GB/s")
+    traffic = traffic_record()
+
+    result = {
+        "metric": "effective weight GB/s (% of HBM peak) for INT4/INT8 GEMV + MoE FFN; "
+                  "prefill TFLOP/s",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "dense INT4 g64 GEMV 4096x4096 + INT8 g64 vocab GEMV "
+                               "4096x129280, M=1, fp32 activations ~N(0,1), weights "
+                               "~N(0,0.02), seed 0",
+                   "step_bytes": step_bytes, "hbm_frac": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "gemv_kernel<8,4,4> (vocab 4096x129280)",
+                     "kernel_us": round(vocab_ms * 1e3, 2), "algorithmic_bytes": bytesv},
+    }
+    del W4
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        result["secondary"] = secondary(dsq, synth, torch, np, dev, WV, x, yv)
+    del WV
+    torch.cuda.empty_cache()
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, np)
+    print(json.dumps(result), flush=True)
+
+
+def secondary(dsq, synth, torch, np, dev, WV, x, yv):
+    out = []
+    K = 4096
+
+    def rotated_gemv(bits, group, name, copies):
+        Ws = []
+        for c in range(copies):
+            w = synth.normal((4096, K), 0.02, 0, synth.W, 100 + c, device=dev)
+            q = dsq.QWeight(bits, group, K, 4096)
+            dsq.pack_weights(w, q)
+            Ws.append(q)
+        del w
+        y = torch.empty(4096, device=dev)
+        ms = time_calls(lambda i: dsq.gemv(Ws[i % copies], x, y), 400, 64, torch)
+        b = qbytes(bits, group, K, 4096) + K * 4 + 4096 * 4
+        gbs = b / (ms * 1e-3) / 1e9
+        out.append({"workload": name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "note": f"rotating {copies} weight copies ({copies * b / 1e6:.0f} MB) "
+                            "so the Infinity Cache cannot hold them"})
+        log(out[-1])
+
+    rotated_gemv(8, 64, "INT8 g64 GEMV 4096x4096 (M=1)", 64)
+    rotated_gemv(4, 64, "INT4 g64 GEMV 4096x4096 (M=1)", 64)
+    torch.cuda.empty_cache()
+
+    # MoE decode layers: 256 experts, H=4096, I=2048, top-6
+    def build_moe(bits, group, bias_std):
+        E, H, I = 256, 4096, 2048
+        router = synth.normal((E, H), 0.02, 0, synth.ROUTER, 0, device=dev)
+        bias = None if bias_std is None else synth.normal((E,), bias_std, 0, synth.BIAS, 0,
+                                                          device=dev)
+        g, u, d = dsq.QWeight(bits, group, H, I, E), dsq.QWeight(bits, group, H, I, E), \
+            dsq.QWeight(bits, group, I, H, E)
+        for e in range(E):
+            wg, wu, wd = synth.expert_weights(e, H, I, 0, device=dev)
+            dsq.pack_weights(wg, g, first=e)
+            dsq.pack_weights(wu, u, first=e)
+            dsq.pack_weights(wd, d, first=e)
+        torch.cuda.synchronize()
+        return router, bias, g, u, d
+
+    def moe_case(name, layer, T, nsets, math, bits, group, iters):
+        H = 4096
+        Xs = [synth.normal((T, H), 1.0, 0, synth.X, 1000 + T * 100 + s, device=dev)
+              for s in range(nsets)]
+        ws = torch.empty(dsq.moe_workspace_bytes(T, 256, 6, H, 2048, math) + 256,
+                         dtype=torch.uint8, device=dev)
+        Y = torch.empty((T, H), device=dev)
+        counts = torch.empty(256, dtype=torch.int32, device=dev)
+        touched = []
+        for s in range(nsets):
+            dsq.moe_ffn(layer, Xs[s], math=math, Y=Y, workspace=ws, counts_out=counts)
+            touched.append(int((counts > 0).sum().item()))
+        D = float(np.mean(touched))
+        ms = time_calls(lambda i: dsq.moe_ffn(layer, Xs[i % nsets], math=math, Y=Y,
+                                              workspace=ws), iters, 4, torch)
+        eb = 3 * qbytes(bits, group, H, 2048)
+        b = 256 * H * 4 + D * eb + 2 * T * H * 4
+        flops = 2 * T * 256 * H + 2 * T * 6 * 3 * H * 2048
+        gbs = b / (ms * 1e-3) / 1e9
+        rec = {"workload": name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "experts_touched": D,
+               "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 3)}
+        out.append(rec)
+        log(rec)
+
+    r, b, g, u, d = build_moe(4, 64, None)
+    moe_case("MoE decode T=1, 256 experts top-6, INT4 g64 SwiGLU",
+             dsq.MoeLayer(r, g, u, d, None, 6), 1, 64, dsq.MATH_FP32, 4, 64, 64)
+    bias = synth.normal((256,), 1.0, 0, synth.BIAS, 0, device=dev)
+    moe_case("MoE batched decode T=32 skewed (router bias ~N(0,1)), INT4 g64",
+             dsq.MoeLayer(r, g, u, d, bias, 6), 32, 8, dsq.MATH_FP32, 4, 64, 16)
+    del g, u, d
+    torch.cuda.empty_cache()
+
+    # dense prefill GEMM M=256, INT8 g128, bf16 MFMA, rotating 32 weight copies
+    Ws = []
+    for c in range(32):
+        w = synth.normal((4096, K), 0.02, 0, synth.W, 200 + c, device=dev)
+        q = dsq.QWeight(8, 128, K, 4096)
+        dsq.pack_weights(w, q)
+        Ws.append(q)
+    del w
+    X = synth.normal((256, K), 1.0, 0, synth.X, 5, device=dev)
+    Y = torch.empty((256, 4096), device=dev)
+    wsb = torch.empty(dsq.gemm_workspace_bytes(256, K, dsq.MATH_BF16_MFMA) + 256,
+                      dtype=torch.uint8, device=dev)
+    ms = time_calls(lambda i: dsq.gemm(Ws[i % 32], X, Y, math=dsq.MATH_BF16_MFMA, workspace=wsb),
+                    128, 16, torch)
+    flops = 2 * 256 * 4096 * K
+    tf = flops / (ms * 1e-3) / 1e12
+    rec = {"workload": "dense prefill GEMM M=256 K=N=4096 INT8 g128 bf16 MFMA",
+           "us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+           "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+           "GB/s": round((qbytes(8, 128, K, 4096) + 2 * 256 * K * 4) / (ms * 1e-3) / 1e9, 1)}
+    out.append(rec)
+    log(rec)
+    del Ws
+    torch.cuda.empty_cache()
+
+    r, b, g, u, d = build_moe(8, 128, None)
+    moe_case("MoE prefill T=256, 256 experts top-6, INT8 g128 SwiGLU, bf16 MFMA",
+             dsq.MoeLayer(r, g, u, d, None, 6), 256, 1, dsq.MATH_BF16_MFMA, 8, 128, 8)
+    del g, u, d
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(seconds, np):
+    """The oracle's fp32 fused-dequant OpenMP GEMV (the pages' CPU method) on
+    a bounded sample of the headline workload: the whole INT4 4096x4096
+    matrix plus the first 16384 rows of the INT8 vocab matrix."""
+    import oracle
+    from group_quantized_moe_dsq_amd import synth
+
+    threads = max(1, (os.cpu_count() or 2) - 1)
+    threads = min(threads, 16)
+    oracle.set_threads(threads)
+    K = 4096
+    rows_v = 16384
+    w4 = synth.normal((4096, K), 0.02, 0, synth.W, 21).numpy()
+    wv = synth.normal((rows_v, K), 0.02, 0, synth.W, 22).numpy()
+    m4 = oracle.quantize(w4, 4, 64)
+    mv = oracle.quantize(wv, 8, 64)
+    del w4, wv
+    x = synth.normal((1, K), 1.0, 0, synth.X, 21).numpy()
+    sample_bytes = qbytes(4, 64, K, 4096) + qbytes(8, 64, K, rows_v) + 2 * K * 4 + \
+        (4096 + rows_v) * 4
+    oracle.qmatmul_f32(x, m4)
+    oracle.qmatmul_f32(x, mv)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.qmatmul_f32(x, m4)
+        oracle.qmatmul_f32(x, mv)
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = (time.perf_counter() - t0) / n
+    return {"value": round(sample_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"INT4 g64 4096x4096 + first {rows_v} rows of the INT8 g64 vocab matrix, "
+                      f"M=1; {n} passes in {seconds:.0f} s; fp32 fused dequant, OpenMP "
+                      f"{threads} threads"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,326 @@
+// api.hip -- the C ABI of libdsq (declared in include/dsq.h).
+//
+// Every entry point validates its arguments on the host first (the
+// up-front shape validation of "ds4 code walkthrough", Part 1, trace 5),
+// returns a status instead of exiting, allocates nothing (callers pass
+// workspace; the same walkthrough forbids allocation in the token loop) and
+// only enqueues kernels on the caller's stream.
+#include <string.h>
+
+#include "common.h"
+#include "internal.h"
+
+using namespace dsq;
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t lim = int64_t(1) << 62) {
+  return a >= 0 && b >= 0 && (a == 0 || b <= lim / a);
+}
+
+// Shape rules of a packed weight (without the pointer).
+dsq_status check_shape(int32_t bits, int32_t group, int64_t K, int64_t N, int64_t batch) {
+  if (bits != 8 && bits != 4) return DSQ_ERR_INVALID_ARG;
+  if (group != 64 && group != 128) return DSQ_ERR_INVALID_ARG;
+  if (K <= 0 || N <= 0 || batch <= 0) return DSQ_ERR_SHAPE;
+  if (K % group != 0) return DSQ_ERR_SHAPE;
+  if (K > kMaxDim || N > kMaxDim || batch > kMaxDim) return DSQ_ERR_OVERFLOW;
+  if (!mul_ok(K, N) || !mul_ok(K * N, batch)) return DSQ_ERR_OVERFLOW;
+  return DSQ_OK;
+}
+
+dsq_status check_qweight(const dsq_qweight* W) {
+  if (!W || !W->data) return DSQ_ERR_INVALID_ARG;
+  const dsq_status s = check_shape(W->bits, W->group, W->K, W->N, W->batch);
+  if (s != DSQ_OK) return s;
+  if (W->layout_version != DSQ_LAYOUT_VERSION || W->reserved != 0) return DSQ_ERR_LAYOUT;
+  if (!aligned(W->data, 256)) return DSQ_ERR_ALIGN;
+  return DSQ_OK;
+}
+
+dsq_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return DSQ_OK;
+  if (e == hipErrorNoDevice || e == hipErrorInvalidDevice) return DSQ_ERR_NO_DEVICE;
+  return DSQ_ERR_HIP;
+}
+
+dsq_status check_device() {
+  int d = -1;
+  const hipError_t e = hipGetDevice(&d);
+  if (e != hipSuccess) return hip_status(e) == DSQ_ERR_HIP ? DSQ_ERR_NO_DEVICE : hip_status(e);
+  return DSQ_OK;
+}
+
+// Carves consecutive 256-byte aligned regions out of a workspace.
+struct Carver {
+  uint8_t* base;
+  int64_t used = 0;
+  bool overflow = false;
+  explicit Carver(void* b) : base(static_cast<uint8_t*>(b)) {}
+  void* take(int64_t n, int64_t elem) {
+    if (!mul_ok(n, elem)) {
+      overflow = true;
+      return nullptr;
+    }
+    void* p = base ? base + used : nullptr;
+    used += align256(n * elem);
+    return p;
+  }
+};
+
+bool use_bf16(int32_t math, int64_t M) {
+  return math == DSQ_MATH_BF16_MFMA || (math == DSQ_MATH_AUTO && M >= 64);
+}
+
+struct MoeWs {
+  float* logits;
+  int32_t* idx;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* pos;
+  int32_t* active;
+  int32_t* n_active;
+  uint32_t* bitmap;
+  void* hbuf;
+  float* ybuf;
+  uint16_t* xb;
+};
+
+int64_t moe_layout(void* ws, int64_t T, int32_t E, int32_t k, int64_t H, int64_t I, bool bf16,
+                   MoeWs* out, bool* overflow) {
+  Carver c(ws);
+  MoeWs m{};
+  const int64_t nk = T * k;
+  m.logits = static_cast<float*>(c.take(T * E, 4));
+  m.idx = static_cast<int32_t*>(c.take(nk, 4));
+  m.w = static_cast<float*>(c.take(nk, 4));
+  m.counts = static_cast<int32_t*>(c.take(E, 4));
+  m.offsets = static_cast<int32_t*>(c.take(E + 1, 4));
+  m.perm = static_cast<int32_t*>(c.take(nk, 4));
+  m.pos = static_cast<int32_t*>(c.take(nk, 4));
+  m.active = static_cast<int32_t*>(c.take(E, 4));
+  m.n_active = static_cast<int32_t*>(c.take(1, 4));
+  m.bitmap = static_cast<uint32_t*>(c.take(int64_t(E) * ((T + 31) / 32), 4));
+  m.hbuf = c.take(nk * I, bf16 ? 2 : 4);
+  m.ybuf = static_cast<float*>(c.take(nk * H, 4));
+  m.xb = bf16 ? static_cast<uint16_t*>(c.take(T * H, 2)) : nullptr;
+  if (out) *out = m;
+  if (overflow) *overflow = c.overflow;
+  return c.used;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dsq_status_string(dsq_status s) {
+  switch (s) {
+    case DSQ_OK: return "DSQ_OK";
+    case DSQ_ERR_INVALID_ARG: return "DSQ_ERR_INVALID_ARG: null pointer or value out of range";
+    case DSQ_ERR_SHAPE: return "DSQ_ERR_SHAPE: inconsistent or unsupported shape";
+    case DSQ_ERR_ALIGN: return "DSQ_ERR_ALIGN: pointer not aligned as required";
+    case DSQ_ERR_WORKSPACE: return "DSQ_ERR_WORKSPACE: workspace missing or too small";
+    case DSQ_ERR_UNSUPPORTED: return "DSQ_ERR_UNSUPPORTED: outside the implemented limits";
+    case DSQ_ERR_NO_DEVICE: return "DSQ_ERR_NO_DEVICE: no HIP device";
+    case DSQ_ERR_HIP: return "DSQ_ERR_HIP: HIP runtime or launch failure";
+    case DSQ_ERR_OVERFLOW: return "DSQ_ERR_OVERFLOW: size computation overflows";
+    case DSQ_ERR_LAYOUT: return "DSQ_ERR_LAYOUT: unknown packed layout version";
+    default: return "unknown dsq_status";
+  }
+}
+
+size_t dsq_packed_bytes(int32_t bits, int32_t group, int64_t K, int64_t N, int64_t batch) {
+  if (check_shape(bits, group, K, N, batch) != DSQ_OK) return 0;
+  const Layout L = layout_of(bits, group, K, N);
+  if (!mul_ok(L.stride, batch)) return 0;
+  return size_t(L.stride * batch);
+}
+
+dsq_status dsq_qweight_init(dsq_qweight* w, int32_t bits, int32_t group, int64_t K, int64_t N,
+                            int64_t batch, void* data) {
+  if (!w || !data) return DSQ_ERR_INVALID_ARG;
+  const dsq_status s = check_shape(bits, group, K, N, batch);
+  if (s != DSQ_OK) return s;
+  if (!aligned(data, 256)) return DSQ_ERR_ALIGN;
+  w->bits = bits;
+  w->group = group;
+  w->K = K;
+  w->N = N;
+  w->batch = batch;
+  w->layout_version = DSQ_LAYOUT_VERSION;
+  w->reserved = 0;
+  w->data = data;
+  return DSQ_OK;
+}
+
+dsq_status dsq_pack_weights(const float* src, const dsq_qweight* out, int64_t first,
+                            int64_t count, int32_t* dev_flags, void* stream) {
+  if (!src) return DSQ_ERR_INVALID_ARG;
+  dsq_status s = check_qweight(out);
+  if (s != DSQ_OK) return s;
+  if (first < 0 || count < 0 || first > out->batch || count > out->batch - first)
+    return DSQ_ERR_INVALID_ARG;
+  if (!aligned(src, 16)) return DSQ_ERR_ALIGN;
+  if (dev_flags && !aligned(dev_flags, 4)) return DSQ_ERR_ALIGN;
+  if ((s = check_device()) != DSQ_OK) return s;
+  return hip_status(launch_pack(src, *out, first, count, dev_flags, (hipStream_t)stream));
+}
+
+dsq_status dsq_gemv(const dsq_qweight* W, int64_t expert, const float* x, float* y,
+                    void* stream) {
+  dsq_status s = check_qweight(W);
+  if (s != DSQ_OK) return s;
+  if (!x || !y) return DSQ_ERR_INVALID_ARG;
+  if (expert < 0 || expert >= W->batch) return DSQ_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 4)) return DSQ_ERR_ALIGN;
+  if ((s = check_device()) != DSQ_OK) return s;
+  return hip_status(launch_gemv(*W, expert, x, y, (hipStream_t)stream));
+}
+
+size_t dsq_gemm_workspace_bytes(int64_t M, int64_t K, int32_t math) {
+  if (M < 0 || K <= 0) return 0;
+  if (math != DSQ_MATH_FP32 && math != DSQ_MATH_BF16_MFMA && math != DSQ_MATH_AUTO) return 0;
+  if (!use_bf16(math, M)) return 0;
+  if (!mul_ok(M, K)) return 0;
+  return size_t(align256(M * K * 2));
+}
+
+dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float* Y, int64_t M,
+                    int32_t math, void* workspace, size_t workspace_bytes, void* stream) {
+  dsq_status s = check_qweight(W);
+  if (s != DSQ_OK) return s;
+  if (!X || !Y) return DSQ_ERR_INVALID_ARG;
+  if (expert < 0 || expert >= W->batch) return DSQ_ERR_INVALID_ARG;
+  if (math != DSQ_MATH_FP32 && math != DSQ_MATH_BF16_MFMA && math != DSQ_MATH_AUTO)
+    return DSQ_ERR_INVALID_ARG;
+  if (M < 0) return DSQ_ERR_SHAPE;
+  if (M > kMaxDim || !mul_ok(M, W->K) || !mul_ok(M, W->N)) return DSQ_ERR_OVERFLOW;
+  if (!aligned(X, 16) || !aligned(Y, 4)) return DSQ_ERR_ALIGN;
+  const bool bf16 = use_bf16(math, M);
+  if (bf16) {
+    const size_t need = dsq_gemm_workspace_bytes(M, W->K, math);
+    if (!workspace || workspace_bytes < need) return DSQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return DSQ_ERR_ALIGN;
+  }
+  if (M == 0) return DSQ_OK;
+  if ((s = check_device()) != DSQ_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  if (!bf16) {
+    if (M == 1) return hip_status(launch_gemv(*W, expert, X, Y, st));
+    return hip_status(
+        launch_smallm_f32(*W, nullptr, expert, nullptr, XR_DENSE, X, M, Y, W->N, st));
+  }
+  uint16_t* xb = static_cast<uint16_t*>(workspace);
+  hipError_t e = launch_to_bf16(X, M * W->K, xb, st);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_mfma_gemm(*W, nullptr, expert, nullptr, XR_DENSE, xb, M, Y, 0, W->N, st));
+}
+
+dsq_status dsq_moe_route_topk(const float* logits, const float* bias, int64_t T, int32_t E,
+                              int32_t top_k, int32_t* idx, float* weights, void* stream) {
+  if (!logits || !idx || !weights) return DSQ_ERR_INVALID_ARG;
+  if (T < 0 || E <= 0 || top_k <= 0 || top_k > E) return DSQ_ERR_SHAPE;
+  if (E > 4096 || top_k > 32 || T > kMaxDim) return DSQ_ERR_UNSUPPORTED;
+  if (!aligned(logits, 4) || !aligned(idx, 4) || !aligned(weights, 4) ||
+      (bias && !aligned(bias, 4)))
+    return DSQ_ERR_ALIGN;
+  if (T == 0) return DSQ_OK;
+  dsq_status s = check_device();
+  if (s != DSQ_OK) return s;
+  return hip_status(launch_topk(logits, bias, T, E, top_k, idx, weights, (hipStream_t)stream));
+}
+
+size_t dsq_moe_workspace_bytes(int64_t T, int32_t E, int32_t top_k, int64_t H, int64_t I,
+                               int32_t math) {
+  if (T < 0 || E <= 0 || top_k <= 0 || top_k > E || H <= 0 || I <= 0) return 0;
+  if (math != DSQ_MATH_FP32 && math != DSQ_MATH_BF16_MFMA && math != DSQ_MATH_AUTO) return 0;
+  if (T > 65536 || E > 4096 || top_k > 32 || H > kMaxDim || I > kMaxDim) return 0;
+  bool ovf = false;
+  const int64_t n = moe_layout(nullptr, T, E, top_k, H, I, use_bf16(math, T), nullptr, &ovf);
+  return ovf ? 0 : size_t(n);
+}
+
+dsq_status dsq_moe_ffn(const float* X, const float* router_w, const float* bias,
+                       const dsq_qweight* gate, const dsq_qweight* up, const dsq_qweight* down,
+                       int64_t T, int32_t top_k, int32_t math, float* Y, void* workspace,
+                       size_t workspace_bytes, float* logits_out, int32_t* idx_out,
+                       float* w_out, int32_t* expert_counts_out, void* stream) {
+  if (!X || !router_w || !Y) return DSQ_ERR_INVALID_ARG;
+  dsq_status s;
+  if ((s = check_qweight(gate)) != DSQ_OK) return s;
+  if ((s = check_qweight(up)) != DSQ_OK) return s;
+  if ((s = check_qweight(down)) != DSQ_OK) return s;
+  if (math != DSQ_MATH_FP32 && math != DSQ_MATH_BF16_MFMA && math != DSQ_MATH_AUTO)
+    return DSQ_ERR_INVALID_ARG;
+  const int64_t E64 = gate->batch;
+  const int64_t H = gate->K, I = gate->N;
+  if (up->batch != E64 || down->batch != E64) return DSQ_ERR_SHAPE;
+  if (up->K != H || up->N != I || down->K != I || down->N != H) return DSQ_ERR_SHAPE;
+  if (up->bits != gate->bits || down->bits != gate->bits || up->group != gate->group ||
+      down->group != gate->group)
+    return DSQ_ERR_SHAPE;
+  if (T < 0 || top_k <= 0 || top_k > E64) return DSQ_ERR_SHAPE;
+  if (T > 65536 || E64 > 4096 || top_k > 32) return DSQ_ERR_UNSUPPORTED;
+  const int32_t E = int32_t(E64);
+  if (!aligned(X, 16) || !aligned(router_w, 16) || !aligned(Y, 16) || (bias && !aligned(bias, 4)))
+    return DSQ_ERR_ALIGN;
+  if ((logits_out && !aligned(logits_out, 4)) || (idx_out && !aligned(idx_out, 4)) ||
+      (w_out && !aligned(w_out, 4)) || (expert_counts_out && !aligned(expert_counts_out, 4)))
+    return DSQ_ERR_ALIGN;
+  const bool bf16 = use_bf16(math, T);
+  const size_t need = dsq_moe_workspace_bytes(T, E, top_k, H, I, math);
+  if (need == 0) return DSQ_ERR_OVERFLOW;
+  if (!workspace || workspace_bytes < need) return DSQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return DSQ_ERR_ALIGN;
+  if (T == 0) return DSQ_OK;
+  if ((s = check_device()) != DSQ_OK) return s;
+
+  MoeWs m{};
+  moe_layout(workspace, T, E, top_k, H, I, bf16, &m, nullptr);
+  if (logits_out) m.logits = logits_out;
+  if (idx_out) m.idx = idx_out;
+  if (w_out) m.w = w_out;
+  if (expert_counts_out) m.counts = expert_counts_out;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e;
+#define DSQ_TRY(call)                          \
+  if ((e = (call)) != hipSuccess) return hip_status(e);
+  // (1) router logits, fp32, bias included
+  DSQ_TRY(launch_router(X, T, router_w, bias, E, H, m.logits, st));
+  // (2) softmax + top-k + renormalisation
+  DSQ_TRY(launch_topk(m.logits, nullptr, T, E, top_k, m.idx, m.w, st));
+  // (3) stable grouping by expert
+  DSQ_TRY(launch_group(m.idx, T, top_k, E, m.bitmap, m.counts, m.offsets, m.perm, m.pos, m.active,
+                       m.n_active, st));
+  Groups g{};
+  g.active = m.active;
+  g.n_active = m.n_active;
+  g.offsets = m.offsets;
+  g.perm = m.perm;
+  g.top_k = top_k;
+  const int64_t max_items = T * top_k < E64 ? T * top_k : E64;
+  g.max_items = int32_t(max_items);
+  // (4) expert FFNs over their token groups, (5) weighted combine
+  if (bf16) {
+    DSQ_TRY(launch_to_bf16(X, T * H, m.xb, st));
+    DSQ_TRY(launch_mfma_gemm(*gate, up, 0, &g, XR_GATHER, m.xb, 0, m.hbuf, 1, I, st));
+    DSQ_TRY(launch_mfma_gemm(*down, nullptr, 0, &g, XR_SEGMENT,
+                             static_cast<const uint16_t*>(m.hbuf), 0, m.ybuf, 0, H, st));
+  } else {
+    DSQ_TRY(launch_smallm_f32(*gate, up, 0, &g, XR_GATHER, X, 0, static_cast<float*>(m.hbuf), I,
+                              st));
+    DSQ_TRY(launch_smallm_f32(*down, nullptr, 0, &g, XR_SEGMENT, static_cast<float*>(m.hbuf), 0,
+                              m.ybuf, H, st));
+  }
+  DSQ_TRY(launch_combine(m.ybuf, m.pos, m.w, T, top_k, H, Y, st));
+#undef DSQ_TRY
+  return DSQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,218 @@
+// gemv.hip -- fused-dequant GEMV for one activation vector (decode, M = 1).
+//
+// Computes y[n] = sum_k x[k] * (q[n][k] - zp[n][g]) * scale[n][g], the
+// matmul with dequantization folded into its inner loop ("Hand-writing a
+// DeepSeek inference engine in pure C", hnwysp.cn/news/134870, §3.2 and
+// §3.3).  The loop is HBM-bound: every weight byte is read once.
+//
+// Mapping (wave64):
+//   * A row is split into 16-byte chunks; lane l of a wave takes chunks
+//     l, l+64, l+128, ...  A wave's load instruction therefore covers 1 KiB
+//     of one row, contiguous, and every lane sees the same K positions for
+//     every row, so its slice of x is loaded into registers once per wave and
+//     reused for all the rows the wave visits (no LDS, no barrier).
+//   * A 16-byte chunk never straddles a quantization group (groups are 32,
+//     64 or 128 bytes and chunk offsets are 16-aligned), so the zero point is
+//     factored per chunk:  sum_c x*(q - zp)*s = s * (sum_c x*q - zp * sum_c x)
+//     with sum_c x precomputed per lane.  Per code that leaves one convert and
+//     one FMA.
+//   * R rows are in flight per wave; their partial sums are reduced across the
+//     wave in one reduce-scatter, after which R lanes store the R outputs.
+#include "common.h"
+#include "internal.h"
+
+namespace dsq {
+
+template <int BITS, int R, int KCH>
+__global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ payload,
+                                                   const float2* __restrict__ meta,
+                                                   const float* __restrict__ x,
+                                                   float* __restrict__ y, int N, int K,
+                                                   int group) {
+  constexpr int EPC = Codes<BITS>::kPerChunk;  // codes per 16-byte chunk
+  const int lane = threadIdx.x & 63;
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int nwaves = (gridDim.x * blockDim.x) >> 6;
+  const int row_bytes = K * BITS / 8;
+  const int nchunk = row_bytes / 16;
+  const int groups = K / group;
+
+  // This lane's slice of x: chunk i covers x[(lane + 64 i) * EPC ...].
+  float xr[KCH][EPC];
+  float xs[KCH];
+#pragma unroll
+  for (int i = 0; i < KCH; ++i) {
+    const int c = lane + 64 * i;
+    xs[i] = 0.0f;
+    if (c < nchunk) {
+      const float4* x4 = reinterpret_cast<const float4*>(x + c * EPC);
+#pragma unroll
+      for (int j = 0; j < EPC / 4; ++j) {
+        const float4 v = x4[j];
+        xr[i][4 * j + 0] = v.x;
+        xr[i][4 * j + 1] = v.y;
+        xr[i][4 * j + 2] = v.z;
+        xr[i][4 * j + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) xr[i][e] = 0.0f;
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) s += xr[i][e];
+    xs[i] = s;
+  }
+
+  for (int rb = wave; rb * R < N; rb += nwaves) {
+    uint4 w[R][KCH];
+    float2 m[R][KCH];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(rb * R + r, N - 1);
+      const uint4* prow = reinterpret_cast<const uint4*>(payload + int64_t(row) * row_bytes);
+      const float2* mrow = meta + int64_t(row) * groups;
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) {
+        const int c = lane + 64 * i;
+        if (c < nchunk) {
+          w[r][i] = ld_nt(prow + c);
+          m[r][i] = mrow[(c * EPC) / group];
+        } else {
+          w[r][i] = make_uint4(0, 0, 0, 0);
+          m[r][i] = make_float2(0.0f, 0.0f);
+        }
+      }
+    }
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      acc[r] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < KCH; ++i) {
+        float f[EPC];
+        Codes<BITS>::unpack(w[r][i], f);
+        // two interleaved chains for ILP
+        float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPC; e += 2) {
+          d0 = fmaf(xr[i][e], f[e], d0);
+          d1 = fmaf(xr[i][e + 1], f[e + 1], d1);
+        }
+        const float d = d0 + d1;
+        acc[r] = fmaf(m[r][i].x, fmaf(-m[r][i].y, xs[i], d), acc[r]);
+      }
+    }
+    const float tot = wave_reduce_scatter<R>(acc);
+    if ((lane & (64 / R - 1)) == 0) {
+      const int row = rb * R + reduce_scatter_row<R>(lane);
+      if (row < N) y[row] = tot;
+    }
+  }
+}
+
+// Rows longer than KMAX chunks per lane: x is re-read from memory (L1/L2)
+// for every chunk instead of being held in registers.
+template <int BITS, int R>
+__global__ __launch_bounds__(256) void gemv_kernel_long(const uint8_t* __restrict__ payload,
+                                                        const float2* __restrict__ meta,
+                                                        const float* __restrict__ x,
+                                                        float* __restrict__ y, int N, int K,
+                                                        int group) {
+  constexpr int EPC = Codes<BITS>::kPerChunk;
+  const int lane = threadIdx.x & 63;
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int nwaves = (gridDim.x * blockDim.x) >> 6;
+  const int row_bytes = K * BITS / 8;
+  const int nchunk = row_bytes / 16;
+  const int groups = K / group;
+  for (int rb = wave; rb * R < N; rb += nwaves) {
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+    for (int c = lane; c < nchunk; c += 64) {
+      float xv[EPC];
+      const float4* x4 = reinterpret_cast<const float4*>(x + c * EPC);
+      float xsum = 0.0f;
+#pragma unroll
+      for (int j = 0; j < EPC / 4; ++j) {
+        const float4 v = x4[j];
+        xv[4 * j] = v.x;
+        xv[4 * j + 1] = v.y;
+        xv[4 * j + 2] = v.z;
+        xv[4 * j + 3] = v.w;
+      }
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) xsum += xv[e];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = min(rb * R + r, N - 1);
+        const uint4 wv = ld_nt(reinterpret_cast<const uint4*>(payload + int64_t(row) * row_bytes) + c);
+        const float2 mv = meta[int64_t(row) * groups + (c * EPC) / group];
+        float f[EPC];
+        Codes<BITS>::unpack(wv, f);
+        float d = 0.0f;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) d = fmaf(xv[e], f[e], d);
+        acc[r] = fmaf(mv.x, fmaf(-mv.y, xsum, d), acc[r]);
+      }
+    }
+    const float tot = wave_reduce_scatter<R>(acc);
+    if ((lane & (64 / R - 1)) == 0) {
+      const int row = rb * R + reduce_scatter_row<R>(lane);
+      if (row < N) y[row] = tot;
+    }
+  }
+}
+
+namespace {
+
+constexpr int kMaxWaves = 256 * 8;  // 8 waves per CU at most, grid-stride beyond
+
+template <int BITS, int R, int KCH>
+hipError_t go(const QMat& q, const float* x, float* y, int N, int K, int group,
+              hipStream_t stream) {
+  const int rowblocks = (N + R - 1) / R;
+  const int waves = rowblocks < kMaxWaves ? rowblocks : kMaxWaves;
+  const int blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((gemv_kernel<BITS, R, KCH>), dim3(blocks), dim3(256), 0, stream, q.payload,
+                     q.meta, x, y, N, K, group);
+  return hipGetLastError();
+}
+
+template <int BITS, int R>
+hipError_t go_long(const QMat& q, const float* x, float* y, int N, int K, int group,
+                   hipStream_t stream) {
+  const int rowblocks = (N + R - 1) / R;
+  const int waves = rowblocks < kMaxWaves ? rowblocks : kMaxWaves;
+  const int blocks = (waves + 3) / 4;
+  hipLaunchKernelGGL((gemv_kernel_long<BITS, R>), dim3(blocks), dim3(256), 0, stream, q.payload,
+                     q.meta, x, y, N, K, group);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t dispatch(const QMat& q, const float* x, float* y, int N, int K, int group,
+                    hipStream_t stream) {
+  const int nchunk = K * BITS / 8 / 16;
+  const int kch = (nchunk + 63) / 64;
+  switch (kch) {
+    case 1: return go<BITS, 4, 1>(q, x, y, N, K, group, stream);
+    case 2: return go<BITS, 4, 2>(q, x, y, N, K, group, stream);
+    case 3: return go<BITS, 4, 3>(q, x, y, N, K, group, stream);
+    case 4: return go<BITS, 4, 4>(q, x, y, N, K, group, stream);
+    default: return go_long<BITS, 4>(q, x, y, N, K, group, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const dsq_qweight& W, int64_t expert, const float* x, float* y,
+                       hipStream_t stream) {
+  const QMat q = entry(W, expert);
+  const int N = int(W.N), K = int(W.K);
+  if (W.bits == 8) return dispatch<8>(q, x, y, N, K, W.group, stream);
+  return dispatch<4>(q, x, y, N, K, W.group, stream);
+}
+
+}  // namespace dsq

@@ -1,0 +1,63 @@
+// internal.h -- launchers shared between the kernel files and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dsq.h"
+
+namespace dsq {
+
+hipError_t launch_pack(const float* src, const dsq_qweight& W, int64_t first, int64_t count,
+                       int32_t* flags, hipStream_t stream);
+
+// y = W[expert] x  (M = 1)
+hipError_t launch_gemv(const dsq_qweight& W, int64_t expert, const float* x, float* y,
+                       hipStream_t stream);
+
+// Routing description for the grouped kernels.  In dense mode `active` is
+// NULL and the single "expert" covers tokens 0..M-1.
+struct Groups {
+  const int32_t* active;    // [E] experts with tokens, ascending (NULL: dense)
+  const int32_t* n_active;  // device scalar
+  const int32_t* offsets;   // [E+1] segment starts in perm order
+  const int32_t* perm;      // [T*k] entry j = t*k+i in (expert, j) order
+  int32_t top_k;
+  int32_t max_items;        // grid bound on the number of active experts
+};
+
+// fp32 grouped small-M kernels.
+//  mode STORE : out[row(m)][n] = sum_k x_m[k] W[n][k]
+//  mode SWIGLU: out[row(m)][n] = silu(x_m Wg[n]) * (x_m Wu[n])
+// x rows: dense -> X + m*K ; moe gather -> X + (perm[p]/top_k)*K ;
+//         moe segment -> X + p*K.   out rows: dense -> m ; moe -> p.
+enum XRows { XR_DENSE = 0, XR_GATHER = 1, XR_SEGMENT = 2 };
+
+hipError_t launch_smallm_f32(const dsq_qweight& A, const dsq_qweight* B, int64_t expert,
+                             const Groups* grp, int xrows, const float* X, int64_t M,
+                             float* out, int64_t ld_out, hipStream_t stream);
+
+// fp32 router: logits[t][e] = X[t] . Wr[e] (+ bias[e])
+hipError_t launch_router(const float* X, int64_t T, const float* Wr, const float* bias,
+                         int32_t E, int64_t H, float* logits, hipStream_t stream);
+
+hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
+                       int32_t* idx, float* w, hipStream_t stream);
+
+// Stable grouping of the T*k routing entries by expert (one workgroup).
+hipError_t launch_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, uint32_t* bitmap,
+                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
+                        int32_t* active, int32_t* n_active, hipStream_t stream);
+
+// Y[t][n] = sum_i w[t][i] * ybuf[pos[t*k+i]][n]
+hipError_t launch_combine(const float* ybuf, const int32_t* pos, const float* w, int64_t T,
+                          int32_t k, int64_t H, float* Y, hipStream_t stream);
+
+// bf16 MFMA path
+hipError_t launch_to_bf16(const float* X, int64_t n, uint16_t* out, hipStream_t stream);
+
+hipError_t launch_mfma_gemm(const dsq_qweight& A, const dsq_qweight* B, int64_t expert,
+                            const Groups* grp, int xrows, const uint16_t* Xb, int64_t M,
+                            void* out, int out_bf16, int64_t ld_out, hipStream_t stream);
+
+}  // namespace dsq

@@ -1,0 +1,511 @@
+// smallm.hip -- fp32 fused-dequant GEMM for few activation rows, dense or
+// grouped by expert, plus the fp32 router.
+//
+// Method: "Hand-writing a DeepSeek inference engine in pure C"
+// (hnwysp.cn/news/134870) §3.2 (dequantize inside the matmul loop), §3.3
+// (the matmul), §3.5 (an expert runs once over all tokens routed to it, so
+// its weights are read once per layer; the SwiGLU expert form is the
+// workload's definition).
+//
+// Mapping: a workgroup of 4 waves owns 4*R output rows of one matrix (one
+// expert) and loops over the tokens of that expert in tiles of MT.  K is
+// walked in rounds of 1024: the round's activations of the MT tokens are
+// staged in LDS, and each lane dequantizes 16 consecutive weights of each of
+// its rows once ((q - zp) * scale, fp32) and reuses them for all MT tokens.
+// Partial sums are reduced across the wave in one reduce-scatter.
+#include "common.h"
+#include "internal.h"
+
+namespace dsq {
+
+// 16 consecutive weights of one row, as floats.
+//  BITS 8 : 16 codes, one 16-byte load
+//  BITS 4 : 16 codes, one 8-byte load (two words of layout version 1)
+//  BITS 32: 16 fp32 weights (unquantized router), four 16-byte loads
+template <int BITS>
+__device__ __forceinline__ void load16(const uint8_t* row, const float2* mrow, int chunk,
+                                       int group, float* f) {
+  if constexpr (BITS == 32) {
+    const float4* p = reinterpret_cast<const float4*>(row) + chunk * 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 v = p[j];
+      f[4 * j] = v.x;
+      f[4 * j + 1] = v.y;
+      f[4 * j + 2] = v.z;
+      f[4 * j + 3] = v.w;
+    }
+  } else {
+    const float2 m = mrow[(chunk * 16) / group];
+    if constexpr (BITS == 8) {
+      const uint4 c = ld_nt(reinterpret_cast<const uint4*>(row) + chunk);
+      Codes<8>::unpack(c, f);
+    } else {
+      const uint2 c = ld_nt(reinterpret_cast<const uint2*>(row) + chunk);
+      bytes4_to_float(c.x & 0x0F0F0F0Fu, f + 0);
+      bytes4_to_float((c.x >> 4) & 0x0F0F0F0Fu, f + 4);
+      bytes4_to_float(c.y & 0x0F0F0F0Fu, f + 8);
+      bytes4_to_float((c.y >> 4) & 0x0F0F0F0Fu, f + 12);
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) f[e] = (f[e] - m.y) * m.x;  // exact q - zp, one rounding
+  }
+}
+
+struct SmArgs {
+  const uint8_t* a;        // matrix A of entry 0 (payload)
+  const uint8_t* b;        // matrix B (SwiGLU up) or NULL
+  int64_t stride;          // bytes per batch entry
+  int64_t meta_off;        // offset of (scale, zp) inside an entry
+  int N, K, group;
+  int64_t expert;          // dense mode: batch entry
+  const int32_t* active;   // moe mode
+  const int32_t* n_active;
+  const int32_t* offsets;
+  const int32_t* perm;
+  int top_k;
+  int xrows;
+  const float* X;
+  int64_t M;               // dense mode: number of rows
+  float* out;
+  int64_t ld_out;
+  const float* bias;       // router bias or NULL
+};
+
+constexpr int kRound = 1024;  // K per LDS round: 64 lanes x 16
+
+template <int BITS, int R, int MT, bool SWIGLU>
+__global__ __launch_bounds__(256) void smallm_kernel(SmArgs p) {
+  constexpr int NR = SWIGLU ? 2 * R : R;  // weight rows per wave
+  constexpr int NV = R * MT;              // outputs per wave per token tile
+  __shared__ float4 xs[MT][kRound / 4];
+  __shared__ int64_t tok_x[MT];
+  __shared__ int64_t tok_o[MT];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int n0 = (blockIdx.x * 4 + wv) * R;
+
+  // which matrix and which tokens
+  int64_t e, p0, M;
+  const bool moe = p.active != nullptr;
+  if (moe) {
+    const int a = blockIdx.y;
+    if (a >= *p.n_active) return;  // uniform over the workgroup
+    e = p.active[a];
+    p0 = p.offsets[e];
+    M = p.offsets[e + 1] - p0;
+  } else {
+    e = p.expert;
+    p0 = 0;
+    M = p.M;
+  }
+  const int64_t row_bytes = int64_t(p.K) * BITS / 8;
+  const int64_t groups = BITS == 32 ? 0 : p.K / p.group;
+  const uint8_t* abase = p.a + e * p.stride;
+  const uint8_t* bbase = SWIGLU ? p.b + e * p.stride : nullptr;
+  const float2* ameta = reinterpret_cast<const float2*>(abase + p.meta_off);
+  const float2* bmeta = SWIGLU ? reinterpret_cast<const float2*>(bbase + p.meta_off) : nullptr;
+  const int nrounds = (p.K + kRound - 1) / kRound;
+
+  const int64_t mstart = moe ? 0 : int64_t(blockIdx.y) * MT;
+  const int64_t mstep = moe ? MT : int64_t(gridDim.y) * MT;
+  for (int64_t m0 = mstart; m0 < M; m0 += mstep) {
+    const int mt = int(M - m0 < MT ? M - m0 : MT);
+    __syncthreads();  // previous tile fully consumed
+    if (threadIdx.x < MT) {
+      const int m = threadIdx.x;
+      int64_t xr = 0, orow = 0;
+      if (m < mt) {
+        const int64_t pidx = p0 + m0 + m;
+        if (p.xrows == XR_GATHER) xr = p.perm[pidx] / p.top_k;
+        else xr = pidx;
+        orow = pidx;
+      }
+      tok_x[m] = xr;
+      tok_o[m] = orow;
+    }
+    float acc[NR][MT];
+#pragma unroll
+    for (int j = 0; j < NR; ++j)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[j][m] = 0.0f;
+
+    for (int rd = 0; rd < nrounds; ++rd) {
+      __syncthreads();
+      // stage x[m][rd*1024 .. +1024) with the chunk swizzle described below
+      for (int idx = threadIdx.x; idx < MT * (kRound / 4); idx += 256) {
+        const int m = idx / (kRound / 4);
+        const int k4 = idx % (kRound / 4);
+        const int k = rd * kRound + k4 * 4;
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (m < mt && k < p.K) v = *reinterpret_cast<const float4*>(p.X + tok_x[m] * p.K + k);
+        // lane l's 16 values are float4 slots 4l..4l+3; rotating them by
+        // (l >> 2) spreads 16 lanes' reads over distinct LDS banks
+        const int l = k4 >> 2, j = k4 & 3;
+        xs[m][l * 4 + ((j + (l >> 2)) & 3)] = v;
+      }
+      __syncthreads();
+      const int chunk = rd * 64 + lane;
+      if (chunk * 16 >= p.K) continue;  // this lane has no weights this round
+      float wf[NR][16];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int n = min(n0 + r, p.N - 1);
+        load16<BITS>(abase + n * row_bytes, ameta + n * groups, chunk, p.group, wf[r]);
+        if constexpr (SWIGLU)
+          load16<BITS>(bbase + n * row_bytes, bmeta + n * groups, chunk, p.group, wf[R + r]);
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m >= mt) break;
+        float xv[16];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 v = xs[m][lane * 4 + ((j + (lane >> 2)) & 3)];
+          xv[4 * j] = v.x;
+          xv[4 * j + 1] = v.y;
+          xv[4 * j + 2] = v.z;
+          xv[4 * j + 3] = v.w;
+        }
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+          float d = acc[j][m];
+#pragma unroll
+          for (int q = 0; q < 16; ++q) d = fmaf(xv[q], wf[j][q], d);
+          acc[j][m] = d;
+        }
+      }
+    }
+
+    // reduce and store: value index v = r * MT + m
+    float va[NV];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+      for (int m = 0; m < MT; ++m) va[r * MT + m] = acc[r][m];
+    const float ta = wave_reduce_scatter<NV>(va);
+    float tb = 0.0f;
+    if constexpr (SWIGLU) {
+      float vb[NV];
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int m = 0; m < MT; ++m) vb[r * MT + m] = acc[R + r][m];
+      tb = wave_reduce_scatter<NV>(vb);
+    }
+    if ((lane & (64 / NV - 1)) == 0) {
+      const int v = reduce_scatter_row<NV>(lane);
+      const int r = v / MT, m = v % MT;
+      const int n = n0 + r;
+      if (m < mt && n < p.N) {
+        float o = ta;
+        if constexpr (SWIGLU) o = silu(ta) * tb;
+        if (p.bias) o += p.bias[n];
+        p.out[tok_o[m] * p.ld_out + n] = o;
+      }
+    }
+  }
+}
+
+static hipError_t launch_sm(const SmArgs& a, int bits, bool swiglu, int items, int64_t M,
+                            hipStream_t stream) {
+  const int MT = 8;
+  const int R = 2;
+  const int rowblocks = (a.N + 4 * R - 1) / (4 * R);
+  int gy;
+  if (a.active) {
+    gy = items;
+  } else {
+    int64_t tiles = (M + MT - 1) / MT;
+    gy = int(tiles < 65535 ? tiles : 65535);
+  }
+  if (rowblocks == 0 || gy == 0) return hipSuccess;
+  dim3 grid(rowblocks, gy);
+  if (bits == 8 && !swiglu)
+    hipLaunchKernelGGL((smallm_kernel<8, 2, 8, false>), grid, dim3(256), 0, stream, a);
+  else if (bits == 8 && swiglu)
+    hipLaunchKernelGGL((smallm_kernel<8, 2, 8, true>), grid, dim3(256), 0, stream, a);
+  else if (bits == 4 && !swiglu)
+    hipLaunchKernelGGL((smallm_kernel<4, 2, 8, false>), grid, dim3(256), 0, stream, a);
+  else if (bits == 4 && swiglu)
+    hipLaunchKernelGGL((smallm_kernel<4, 2, 8, true>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((smallm_kernel<32, 2, 8, false>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_smallm_f32(const dsq_qweight& A, const dsq_qweight* B, int64_t expert,
+                             const Groups* grp, int xrows, const float* X, int64_t M,
+                             float* out, int64_t ld_out, hipStream_t stream) {
+  const Layout L = layout_of(A.bits, A.group, A.K, A.N);
+  SmArgs a{};
+  a.a = static_cast<const uint8_t*>(A.data);
+  a.b = B ? static_cast<const uint8_t*>(B->data) : nullptr;
+  a.stride = L.stride;
+  a.meta_off = L.meta_off;
+  a.N = int(A.N);
+  a.K = int(A.K);
+  a.group = A.group;
+  a.expert = expert;
+  a.xrows = xrows;
+  a.X = X;
+  a.M = M;
+  a.out = out;
+  a.ld_out = ld_out;
+  a.bias = nullptr;
+  int items = 1;
+  if (grp) {
+    a.active = grp->active;
+    a.n_active = grp->n_active;
+    a.offsets = grp->offsets;
+    a.perm = grp->perm;
+    a.top_k = grp->top_k;
+    items = grp->max_items;
+  }
+  return launch_sm(a, A.bits, B != nullptr, items, M, stream);
+}
+
+hipError_t launch_router(const float* X, int64_t T, const float* Wr, const float* bias,
+                         int32_t E, int64_t H, float* logits, hipStream_t stream) {
+  SmArgs a{};
+  a.a = reinterpret_cast<const uint8_t*>(Wr);
+  a.b = nullptr;
+  a.stride = 0;
+  a.meta_off = 0;
+  a.N = E;
+  a.K = int(H);
+  a.group = 1;
+  a.expert = 0;
+  a.xrows = XR_DENSE;
+  a.X = X;
+  a.M = T;
+  a.out = logits;
+  a.ld_out = E;
+  a.bias = bias;
+  return launch_sm(a, 32, false, 1, T, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Softmax + top-k + renormalisation ("Hand-writing a DeepSeek inference
+// engine in pure C" §3.4: subtract the maximum; §3.5: top-k by a greater-first
+// sort of (score, index) pairs).  One wave per token; each lane holds EPL
+// scores.  k rounds of a wave-wide argmax with the comparator
+// (score desc, index desc); lane i keeps the i-th winner.  The renormalised
+// weight of a selected expert is exp(s_i - s_max) / sum_sel exp(s_j - s_max):
+// the full softmax denominator cancels in p_i / sum_sel p_j.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia > ib);
+}
+
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+                                                   const float* __restrict__ bias, int T, int E,
+                                                   int k, int32_t* __restrict__ idx,
+                                                   float* __restrict__ wout) {
+  const int lane = threadIdx.x & 63;
+  const int t = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  if (t >= T) return;
+  float v[EPL];
+  uint64_t taken = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane + 64 * j;
+    float s = -INFINITY;
+    if (e < E) {
+      s = logits[int64_t(t) * E + e];
+      if (bias) s += bias[e];
+      if (s != s) s = -INFINITY;  // NaN ranks last
+    } else {
+      taken |= uint64_t(1) << j;  // padding never wins
+    }
+    v[j] = s;
+  }
+  float my_val = 0.0f;
+  int my_idx = 0;
+  float best_val = 0.0f;
+  for (int i = 0; i < k; ++i) {
+    // local best among not-taken
+    float bv = -INFINITY;
+    int bi = -1;
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) {
+      const int e = lane + 64 * j;
+      if (!((taken >> j) & 1) && (bi < 0 || ranks_before(v[j], e, bv, bi))) {
+        bv = v[j];
+        bi = e;
+      }
+    }
+    // wave argmax; lanes without a candidate carry index -1
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (oi >= 0 && (bi < 0 || ranks_before(ov, oi, bv, bi))) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (bi >= 0 && (bi & 63) == lane) taken |= uint64_t(1) << (bi >> 6);
+    if (i == 0) best_val = bv;
+    if (lane == i) {
+      my_val = bv;
+      my_idx = bi;
+    }
+  }
+  const float ex = lane < k ? expf(my_val - best_val) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) {
+    idx[int64_t(t) * k + lane] = my_idx;
+    wout[int64_t(t) * k + lane] = ex / sum;
+  }
+}
+
+hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
+                       int32_t* idx, float* w, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const int64_t blocks = (T + 3) / 4;
+  const int epl = (E + 63) / 64;
+#define DSQ_TOPK(n)                                                                        \
+  hipLaunchKernelGGL(topk_kernel<n>, dim3(unsigned(blocks)), dim3(256), 0, stream, logits, \
+                     bias, int(T), E, k, idx, w)
+  if (epl <= 1) DSQ_TOPK(1);
+  else if (epl <= 2) DSQ_TOPK(2);
+  else if (epl <= 4) DSQ_TOPK(4);
+  else if (epl <= 8) DSQ_TOPK(8);
+  else if (epl <= 16) DSQ_TOPK(16);
+  else if (epl <= 32) DSQ_TOPK(32);
+  else DSQ_TOPK(64);
+#undef DSQ_TOPK
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Grouping by expert (§3.5 of the same page: gather the tokens routed to one
+// expert).  One workgroup.  A token selects distinct experts, so an entry's
+// rank inside its expert's segment is the number of earlier tokens that
+// selected the same expert: a bitmap [E][ceil(T/32)] with bit t of row e set
+// when token t chose e turns that into popcounts.  Integer only, so the
+// result is exact and stable (ascending token order within an expert).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__ idx, int T, int k,
+                                                     int E, uint32_t* __restrict__ bm,
+                                                     int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ perm,
+                                                     int32_t* __restrict__ pos,
+                                                     int32_t* __restrict__ active,
+                                                     int32_t* __restrict__ n_active) {
+  __shared__ int32_t s_off[4097];
+  __shared__ int32_t s_act[4097];
+  const int W = (T + 31) / 32;
+  const int nent = T * k;
+  for (int i = threadIdx.x; i < E * W; i += blockDim.x) bm[i] = 0u;
+  __syncthreads();
+  for (int j = threadIdx.x; j < nent; j += blockDim.x) {
+    const int e = idx[j];
+    const int t = j / k;
+    atomicOr(&bm[e * W + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    int c = 0;
+    const volatile uint32_t* row = bm + e * W;
+    for (int w = 0; w < W; ++w) c += __popc(row[w]);
+    s_off[e] = c;
+  }
+  __syncthreads();
+  // exclusive scans of counts and of (count > 0) by wave 0
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int per = (E + 63) / 64;
+    const int lo = lane * per;
+    const int hi = min(lo + per, E);
+    int sc = 0, sa = 0;
+    for (int e = lo; e < hi; ++e) {
+      sc += s_off[e];
+      sa += s_off[e] > 0;
+    }
+    int ic = sc, ia = sa;  // inclusive scan across lanes
+    for (int o = 1; o < 64; o <<= 1) {
+      const int uc = __shfl_up(ic, o);
+      const int ua = __shfl_up(ia, o);
+      if (lane >= o) {
+        ic += uc;
+        ia += ua;
+      }
+    }
+    int rc = ic - sc, ra = ia - sa;
+    for (int e = lo; e < hi; ++e) {
+      const int c = s_off[e];
+      counts[e] = c;
+      s_off[e] = rc;
+      s_act[e] = ra;
+      offsets[e] = rc;
+      if (c > 0) active[ra] = e;
+      rc += c;
+      ra += c > 0;
+    }
+    if (lane == 63) {
+      offsets[E] = ic;
+      s_off[E] = ic;
+      *n_active = ia;
+    }
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < nent; j += blockDim.x) {
+    const int e = idx[j];
+    const int t = j / k;
+    // the bitmap was built with device-scope atomics: read it past L1
+    const volatile uint32_t* row = bm + e * W;
+    int rank = 0;
+    for (int w = 0; w < (t >> 5); ++w) rank += __popc(row[w]);
+    rank += __popc(row[t >> 5] & ((1u << (t & 31)) - 1u));
+    const int p = s_off[e] + rank;
+    perm[p] = j;
+    pos[j] = p;
+  }
+}
+
+hipError_t launch_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, uint32_t* bitmap,
+                        int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
+                        int32_t* active, int32_t* n_active, hipStream_t stream) {
+  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, stream, idx, int(T), k, E, bitmap,
+                     counts, offsets, perm, pos, active, n_active);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Weighted combine in slot order (§3.5: weighted sum of the expert outputs).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf,
+                                                      const int32_t* __restrict__ pos,
+                                                      const float* __restrict__ w, int T, int k,
+                                                      int H, float* __restrict__ Y) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;  // float4 index
+  const int h4 = H / 4;
+  if (i >= int64_t(T) * h4) return;
+  const int t = int(i / h4), c = int(i % h4);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < k; ++s) {
+    const float ws = w[t * k + s];
+    const float4 v = reinterpret_cast<const float4*>(ybuf + int64_t(pos[t * k + s]) * H)[c];
+    acc.x = fmaf(ws, v.x, acc.x);
+    acc.y = fmaf(ws, v.y, acc.y);
+    acc.z = fmaf(ws, v.z, acc.z);
+    acc.w = fmaf(ws, v.w, acc.w);
+  }
+  reinterpret_cast<float4*>(Y + int64_t(t) * H)[c] = acc;
+}
+
+hipError_t launch_combine(const float* ybuf, const int32_t* pos, const float* w, int64_t T,
+                          int32_t k, int64_t H, float* Y, hipStream_t stream) {
+  const int64_t n = T * (H / 4);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, ybuf,
+                     pos, w, int(T), k, int(H), Y);
+  return hipGetLastError();
+}
+
+}  // namespace dsq

@@ -1,0 +1,211 @@
+/*
+ * dsq.h -- C ABI of libdsq: group-quantized fused-dequant GEMV / GEMM and the
+ * top-k routed mixture-of-experts SwiGLU FFN on AMD MI355X (gfx950).
+ *
+ * The method (all citations name the page and its section):
+ *   "Hand-writing a DeepSeek inference engine in pure C" (hnwysp.cn/news/134870)
+ *     §2.3  weights quantized group-wise (groups of 64 or 128 along the
+ *           reduction axis), asymmetric, dequantized as (q - zero_point) *
+ *           scale; the stored layout must suit the matmul kernel;
+ *     §3.2  scale = (max - min) / (2^bits - 1), zero_point = round(-min /
+ *           scale), q = clamp(round(v / scale) + zero_point, 0, 2^bits - 1);
+ *           INT4 stores two values per byte; scale and zero point are fp32;
+ *           dequantization is fused into the matmul's inner loop;
+ *     §3.3  the matmul;
+ *     §3.4  softmax with the maximum subtracted;
+ *     §3.5  MoE: router = linear layer + softmax, top-k experts, tokens
+ *           grouped by expert so each expert's weights are read once, outputs
+ *           combined by a weighted sum;
+ *     §5.1  a zero scale is an error.
+ *   "ds4 code walkthrough" (ds4-learning.pages.dev), Part 1: every shape is
+ *     validated before use, errors are reported rather than fatal inside
+ *     the library, no allocation inside the token loop.
+ *
+ * Conventions shared by every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates nothing, keeps no state between calls and never synchronises;
+ *     every call only enqueues kernels on `stream` (a hipStream_t, NULL = the
+ *     default stream).  Calls are re-entrant; two calls that share a
+ *     workspace must be ordered on one stream.
+ *   - Arguments are validated on the host before anything is enqueued.  A
+ *     failed check returns a negative dsq_status and enqueues nothing, so no
+ *     output is written.  Launch failures return DSQ_ERR_HIP.
+ *   - Results are deterministic for given inputs on a given device: no
+ *     floating-point atomics anywhere.
+ *   - fp32 tensors are row-major and 16-byte aligned.
+ */
+#ifndef DSQ_H
+#define DSQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t dsq_status;
+#define DSQ_OK 0
+#define DSQ_ERR_INVALID_ARG (-1) /* NULL pointer, value out of range      */
+#define DSQ_ERR_SHAPE (-2)       /* K % group != 0, sizes <= 0, k > E ... */
+#define DSQ_ERR_ALIGN (-3)       /* pointer not aligned as required      */
+#define DSQ_ERR_WORKSPACE (-4)   /* workspace NULL or too small          */
+#define DSQ_ERR_UNSUPPORTED (-5) /* valid but not implemented (limits)   */
+#define DSQ_ERR_NO_DEVICE (-6)   /* no HIP device visible                */
+#define DSQ_ERR_HIP (-7)         /* a HIP runtime call or launch failed  */
+#define DSQ_ERR_OVERFLOW (-8)    /* a size computation overflows         */
+#define DSQ_ERR_LAYOUT (-9)      /* packed buffer has an unknown layout  */
+
+/* Arithmetic of the matmuls. */
+#define DSQ_MATH_FP32 0      /* fp32 products and sums (VALU FMA)              */
+#define DSQ_MATH_BF16_MFMA 1 /* activations and dequantized weights rounded to  */
+                             /* bf16, products summed in fp32 on MFMA           */
+#define DSQ_MATH_AUTO 2      /* BF16_MFMA when the token count M >= 64, else    */
+                             /* FP32                                            */
+
+/* Flags written (OR-ed) into the packer's status word. */
+#define DSQ_FLAG_DEGENERATE 1 /* a group with max == min (scale 0), a scale   */
+                              /* that is not finite, or |zero point| > 2^24   */
+#define DSQ_FLAG_NONFINITE 2  /* a group holding NaN or +-inf                 */
+
+/*
+ * Device layout, version 1 (DSQ_LAYOUT_VERSION).  For a weight W[batch][N][K]
+ * quantized with `bits` and `group`, RB = K * bits / 8 bytes per row:
+ *   per batch entry b, at byte offset b * stride:
+ *     payload : N rows of RB bytes, row-major.
+ *               INT8: byte k of row n is q[n][k] (0..255).
+ *               INT4: the 32-bit little-endian word j of a row holds
+ *                     k = 8j .. 8j+7; its byte i (0..3) holds q[n][8j+i] in
+ *                     the low nibble and q[n][8j+4+i] in the high nibble, so
+ *                     masking the word with 0x0F0F0F0F yields four
+ *                     consecutive codes and shifting by 4 first the next four.
+ *     meta    : at offset align256(N * RB): N rows of K/group pairs
+ *               (float scale, float zero_point); the zero point is an exact
+ *               integer held in fp32.
+ *   stride = align256(N * RB) + align256(N * (K/group) * 8).
+ * A flagged group has all its codes 0 and scale = zero point = 0.
+ */
+#define DSQ_LAYOUT_VERSION 1u
+
+typedef struct dsq_qweight {
+  int32_t bits;            /* 8 or 4                                          */
+  int32_t group;           /* 64 or 128, along K                              */
+  int64_t K;               /* reduction length (columns of W)                 */
+  int64_t N;               /* outputs (rows of W)                             */
+  int64_t batch;           /* number of matrices (experts); 1 for dense       */
+  uint32_t layout_version; /* written by dsq_pack_weights                     */
+  uint32_t reserved;       /* must be 0                                       */
+  void* data;              /* device buffer of dsq_packed_bytes() bytes,      */
+                           /* 256-byte aligned, owned by the caller           */
+} dsq_qweight;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* dsq_status_string(dsq_status s);
+
+/* Bytes of the packed buffer for W[batch][N][K]; 0 if the arguments are
+   invalid (bits, group, K % group, non-positive sizes) or overflow. */
+size_t dsq_packed_bytes(int32_t bits, int32_t group, int64_t K, int64_t N, int64_t batch);
+
+/* Fill a descriptor (layout_version = DSQ_LAYOUT_VERSION, reserved = 0).
+   Validates like dsq_packed_bytes and the 256-byte alignment of data. */
+dsq_status dsq_qweight_init(dsq_qweight* w, int32_t bits, int32_t group, int64_t K, int64_t N,
+                            int64_t batch, void* data);
+
+/*
+ * dsq_pack_weights -- quantize and lay out weights ("quantize once at model
+ * conversion time", hnwysp.cn/news/134870 §3.2 and §2.3).
+ *   src        : fp32 [count][N][K] device, the weights of batch entries
+ *                first .. first+count-1 of `out`.
+ *   out        : descriptor from dsq_qweight_init; out->data receives the
+ *                codes and (scale, zero point) of those entries.
+ *   dev_flags  : optional device int32; DSQ_FLAG_* bits of every flagged
+ *                group of this call are OR-ed into it (the caller zeroes it).
+ *                NULL = do not report.
+ * Quantization per group of `group` consecutive weights along K, in IEEE fp32
+ * with correctly rounded division and round-half-away-from-zero:
+ *   scale = (max - min) / (2^bits - 1); zp = round(-min / scale);
+ *   q = clamp(round(v / scale) + zp, 0, 2^bits - 1).
+ * Errors: DSQ_ERR_INVALID_ARG (NULL src/out/data, first/count out of range),
+ * DSQ_ERR_SHAPE, DSQ_ERR_ALIGN (src not 16-byte or data not 256-byte
+ * aligned), DSQ_ERR_LAYOUT (descriptor version), DSQ_ERR_NO_DEVICE,
+ * DSQ_ERR_HIP.
+ */
+dsq_status dsq_pack_weights(const float* src, const dsq_qweight* out, int64_t first,
+                            int64_t count, int32_t* dev_flags, void* stream);
+
+/*
+ * dsq_gemv -- y = dequant(W[expert]) x for one activation vector (decode,
+ * M = 1), dequantization fused into the reduction (hnwysp.cn/news/134870
+ * §3.2, §3.3):  y[n] = sum_k x[k] * (q[n][k] - zp[n][g]) * scale[n][g].
+ *   W : packed weight (layout 1); expert in [0, W->batch).
+ *   x : fp32 [K] device.   y : fp32 [N] device (written).
+ * fp32 arithmetic; per output |y - exact| <= 1e-5 * sum_k |x[k] w[n][k]|.
+ * Errors: DSQ_ERR_INVALID_ARG, DSQ_ERR_SHAPE, DSQ_ERR_ALIGN, DSQ_ERR_LAYOUT,
+ * DSQ_ERR_NO_DEVICE, DSQ_ERR_HIP.
+ */
+dsq_status dsq_gemv(const dsq_qweight* W, int64_t expert, const float* x, float* y,
+                    void* stream);
+
+/*
+ * dsq_gemm -- Y = X dequant(W[expert])^T for M activation rows (batched
+ * decode and prefill).
+ *   X : fp32 [M][K] device.   Y : fp32 [M][N] device (written).
+ *   math : DSQ_MATH_FP32, DSQ_MATH_BF16_MFMA or DSQ_MATH_AUTO.
+ *   workspace : device scratch of dsq_gemm_workspace_bytes(M, K, math)
+ *               bytes (may be NULL when that is 0), 256-byte aligned.
+ * FP32: |err| <= 1e-5 * sum|x w| per output.  BF16_MFMA: X and the
+ * dequantized weights are rounded to bf16 and products are summed in fp32:
+ * |err| <= 1e-2 * sum|x w| per output.
+ */
+size_t dsq_gemm_workspace_bytes(int64_t M, int64_t K, int32_t math);
+dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float* Y, int64_t M,
+                    int32_t math, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dsq_moe_route_topk -- router softmax + top-k + renormalisation
+ * (hnwysp.cn/news/134870 §3.4, §3.5).
+ *   logits : fp32 [T][E] device;  bias : fp32 [E] device or NULL, added to
+ *            every logit before anything else.
+ *   idx    : int32 [T][top_k] device: the top_k experts by score, highest
+ *            first; equal scores rank the higher expert index first.
+ *   weights: fp32 [T][top_k] device: softmax probabilities of the selected
+ *            experts divided by their sum (so they sum to 1); computed from
+ *            the max-subtracted scores.
+ * Scores must be finite (a NaN is ranked as -infinity).
+ * Limits: 1 <= top_k <= min(E, 32), E <= 4096.
+ */
+dsq_status dsq_moe_route_topk(const float* logits, const float* bias, int64_t T, int32_t E,
+                              int32_t top_k, int32_t* idx, float* weights, void* stream);
+
+/*
+ * dsq_moe_ffn -- one routed MoE layer:
+ *   l = X Wr^T (+ bias)                    router logits, fp32
+ *   (idx, w) = route_topk(l)               as dsq_moe_route_topk
+ *   group the T*top_k entries by expert    stable, ascending token order
+ *   h = silu(X Wg_e^T) * (X Wu_e^T)        per expert, its tokens only
+ *   Y[t] = sum_i w[t][i] * (h Wd_e^T)[t]   summed in slot order i = 0..k-1
+ *   X        : fp32 [T][H] device.     router_w : fp32 [E][H] device.
+ *   bias     : fp32 [E] device or NULL.
+ *   gate, up : packed, batch = E, N = I, K = H.  down : batch = E, N = H,
+ *              K = I.  All three share bits and group.
+ *   math     : as dsq_gemm, choosing by T.  The router is always fp32.
+ *   Y        : fp32 [T][H] device (written).
+ *   workspace: dsq_moe_workspace_bytes(T, E, top_k, H, I, math) bytes,
+ *              256-byte aligned; contents on entry are ignored.
+ *   Optional outputs (NULL to skip): logits_out fp32 [T][E] (including the
+ *   bias), idx_out int32 [T][k], w_out fp32 [T][k], expert_counts_out int32
+ *   [E] (tokens routed to each expert; the pages log overloaded experts).
+ * Limits: T <= 65536, E <= 4096, 1 <= top_k <= min(E, 32).
+ */
+size_t dsq_moe_workspace_bytes(int64_t T, int32_t E, int32_t top_k, int64_t H, int64_t I,
+                               int32_t math);
+dsq_status dsq_moe_ffn(const float* X, const float* router_w, const float* bias,
+                       const dsq_qweight* gate, const dsq_qweight* up, const dsq_qweight* down,
+                       int64_t T, int32_t top_k, int32_t math, float* Y, void* workspace,
+                       size_t workspace_bytes, float* logits_out, int32_t* idx_out,
+                       float* w_out, int32_t* expert_counts_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSQ_H */

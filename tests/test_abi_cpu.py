@@ -1,0 +1,151 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol that
+include/dsq.h declares, and its host logic (size queries, argument
+validation) behaves as documented.  No compute call is made: every call here
+returns from the host-side checks before anything would be enqueued."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import layout_v1
+import oracle
+from group_quantized_moe_dsq_amd import dsq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = dsq.lib()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), f"libdsq.so does not export {n}"
+    assert sorted(dsq.EXPORTS) == names
+
+
+def test_status_strings():
+    for code, name in dsq.STATUS.items():
+        assert dsq.status_string(code).startswith(name)
+    assert dsq.status_string(12345) == "unknown dsq_status"
+
+
+@pytest.mark.parametrize("bits,group,K,N,batch", [(8, 64, 4096, 4096, 1), (4, 64, 4096, 2048, 256),
+                                                   (8, 128, 2048, 4096, 3), (4, 128, 256, 33, 2),
+                                                   (8, 64, 4096, 129280, 1)])
+def test_packed_bytes_matches_layout(bits, group, K, N, batch):
+    assert dsq.packed_bytes(bits, group, K, N, batch) == layout_v1.packed_bytes(bits, group, K, N,
+                                                                                 batch)
+
+
+def test_packed_bytes_rejects():
+    assert dsq.packed_bytes(5, 64, 128, 4, 1) == 0
+    assert dsq.packed_bytes(8, 32, 128, 4, 1) == 0
+    assert dsq.packed_bytes(8, 64, 100, 4, 1) == 0
+    assert dsq.packed_bytes(8, 64, 0, 4, 1) == 0
+    assert dsq.packed_bytes(8, 64, 1 << 40, 1 << 40, 1) == 0
+
+
+def desc(bits=8, group=64, K=128, N=4, batch=1, data=0x10000):
+    d = dsq.QWeightDesc()
+    rc = dsq.lib().dsq_qweight_init(ctypes.byref(d), bits, group, K, N, batch,
+                                    ctypes.c_void_p(data))
+    return d, rc
+
+
+def test_qweight_init_validation():
+    d, rc = desc()
+    assert rc == 0 and d.layout_version == dsq.LAYOUT_VERSION and d.reserved == 0
+    assert desc(data=0x10001)[1] == -3          # not 256-byte aligned
+    assert desc(K=100)[1] == -2                 # K % group
+    assert desc(bits=3)[1] == -1
+    assert desc(data=0)[1] == -1
+
+
+def test_calls_validate_before_touching_the_device():
+    L = dsq.lib()
+    d, _ = desc()
+    fake = ctypes.c_void_p(0x20000)
+    mis = ctypes.c_void_p(0x20004)
+    # NULL pointers
+    assert L.dsq_gemv(None, 0, fake, fake, None) == -1
+    assert L.dsq_gemv(ctypes.byref(d), 0, None, fake, None) == -1
+    # expert out of range
+    assert L.dsq_gemv(ctypes.byref(d), 1, fake, fake, None) == -1
+    # misaligned x
+    assert L.dsq_gemv(ctypes.byref(d), 0, mis, fake, None) == -3
+    # wrong layout version
+    bad = dsq.QWeightDesc.from_buffer_copy(d)
+    bad.layout_version = 7
+    assert L.dsq_gemv(ctypes.byref(bad), 0, fake, fake, None) == -9
+    # gemm: bad math mode, negative M, missing workspace for bf16
+    assert L.dsq_gemm(ctypes.byref(d), 0, fake, fake, 4, 9, None, 0, None) == -1
+    assert L.dsq_gemm(ctypes.byref(d), 0, fake, fake, -1, 0, None, 0, None) == -2
+    assert L.dsq_gemm(ctypes.byref(d), 0, fake, fake, 128, 1, None, 0, None) == -4
+    # pack: range of entries
+    assert L.dsq_pack_weights(fake, ctypes.byref(d), 0, 2, None, None) == -1
+    assert L.dsq_pack_weights(None, ctypes.byref(d), 0, 1, None, None) == -1
+    # route: k > E, unsupported sizes
+    assert L.dsq_moe_route_topk(fake, None, 4, 8, 9, fake, fake, None) == -2
+    assert L.dsq_moe_route_topk(fake, None, 4, 8192, 6, fake, fake, None) == -5
+    assert L.dsq_moe_route_topk(None, None, 4, 8, 2, fake, fake, None) == -1
+
+
+def test_moe_validation_and_workspace_query():
+    L = dsq.lib()
+    H, I, E = 256, 128, 8
+    g, _ = desc(4, 64, H, I, E)
+    u, _ = desc(4, 64, H, I, E)
+    dn, _ = desc(4, 64, I, H, E)
+    fake = ctypes.c_void_p(0x40000)
+    need = dsq.moe_workspace_bytes(5, E, 2, H, I, dsq.MATH_FP32)
+    assert need > 0
+    # workspace too small
+    rc = L.dsq_moe_ffn(fake, fake, None, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), 5, 2,
+                       0, fake, fake, need - 1, None, None, None, None, None)
+    assert rc == -4
+    # mismatched down shape
+    dbad, _ = desc(4, 64, H, H, E)
+    rc = L.dsq_moe_ffn(fake, fake, None, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dbad), 5,
+                       2, 0, fake, fake, need, None, None, None, None, None)
+    assert rc == -2
+    # mixed bit widths
+    u8, _ = desc(8, 64, H, I, E)
+    rc = L.dsq_moe_ffn(fake, fake, None, ctypes.byref(g), ctypes.byref(u8), ctypes.byref(dn), 5,
+                       2, 0, fake, fake, need, None, None, None, None, None)
+    assert rc == -2
+    # k > E
+    rc = L.dsq_moe_ffn(fake, fake, None, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), 5,
+                       9, 0, fake, fake, need, None, None, None, None, None)
+    assert rc == -2
+    # the bf16 workspace holds the bf16 copies in addition
+    assert dsq.moe_workspace_bytes(256, 256, 6, 4096, 2048, dsq.MATH_BF16_MFMA) > 0
+    assert dsq.moe_workspace_bytes(5, E, 9, H, I, 0) == 0
+
+
+def test_layout_decoder_round_trip():
+    """The test-side layout reader inverts its own encoder, and the encoder
+    puts INT4 codes where the header says (word j, byte i: k = 8j+i low,
+    k = 8j+4+i high)."""
+    rng = np.random.default_rng(40)
+    w = (rng.standard_normal((5, 256)) * 0.02).astype(np.float32)
+    for bits in (8, 4):
+        m = oracle.quantize(w, bits, 64)
+        raw = layout_v1.encode_entry(m.q, m.scale, m.zp, bits, 64, 256, 5)
+        q, s, z = layout_v1.decode_entry(raw, 0, bits, 64, 256, 5)
+        np.testing.assert_array_equal(q, m.q)
+        np.testing.assert_array_equal(s, m.scale)
+        np.testing.assert_array_equal(z, m.zp)
+        if bits == 4:
+            codes = oracle.unpack_q(m)
+            word0 = raw[0:4]
+            assert [int(b) & 15 for b in word0] == list(codes[0, 0:4])
+            assert [int(b) >> 4 for b in word0] == list(codes[0, 4:8])

@@ -1,0 +1,161 @@
+"""GPU parity: the whole routed MoE layer (router, top-k, grouping, expert
+SwiGLU GEMMs, weighted combine) against the oracle.
+
+Method: "Hand-writing a DeepSeek inference engine in pure C"
+(hnwysp.cn/news/134870) §3.4-§3.5.  Bounds:
+  logits : |l - l_ref| <= 1e-5 * sum_h |x_h wr_h|  (+ one fp32 rounding of the
+           bias addition);
+  idx    : the same expert set as the oracle's for every token whose oracle
+           margin between the k-th and (k+1)-th logit exceeds twice the logit
+           bound; for the others (near-ties, where both choices are right) the
+           GPU's set must be one of the sets the oracle admits within that
+           bound; slots ordered by the kernel's own fp32 scores;
+  w      : first-order softmax propagation of the logit bound, + 1e-6;
+  Y      : rel * sum_i w_i (S_i + P_i) + sum_i dw_i |y_i|, with S_i the
+           down-projection magnitude sum, P_i the first-order effect of a
+           relative error rel in the gate/up sums (both from the oracle), dw_i
+           the weight bound; rel = 1e-5 (fp32) or 1e-2 (bf16 MFMA).
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import MoeFixture, assert_bounded, assert_normwise, say
+from group_quantized_moe_dsq_amd import dsq, synth
+
+pytestmark = pytest.mark.gpu
+
+
+def run_moe(fx: MoeFixture, X, k, math):
+    T = X.shape[0]
+    lay = fx.layer(k)
+    logits = torch.empty((T, fx.E), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    counts = torch.empty((fx.E,), dtype=torch.int32, device="cuda")
+    Y = dsq.moe_ffn(lay, X, math=math, logits_out=logits, idx_out=idx, w_out=w,
+                    counts_out=counts)
+    Y2 = dsq.moe_ffn(lay, X, math=math)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2), "moe_ffn is not deterministic"
+    return (Y.cpu().numpy(), logits.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy(),
+            counts.cpu().numpy())
+
+
+def check_moe(fx: MoeFixture, X, k, math, rel, tokens=None):
+    T = X.shape[0]
+    Y, L, idx, w, counts = run_moe(fx, X, k, math)
+    Xc = X.cpu().numpy().astype(np.float64)
+    bias = None if fx.bias is None else fx.bias.cpu().numpy().astype(np.float64)
+    Lref, SL = oracle.router_f64(Xc, fx.router.cpu().numpy(), bias)
+    lb = 1e-5 * SL + 2.0 ** -23 * np.abs(Lref)
+    assert_bounded(L, Lref, lb, "router logits")
+
+    ref_idx, ref_w, gap = oracle.route(Lref, k)
+    delta = lb.max(axis=1)
+    clear = gap > 2 * delta
+    say(f"  routing: {int(clear.sum())}/{T} tokens with a clear top-{k} margin")
+    for t in range(T):
+        if clear[t]:
+            assert set(idx[t]) == set(ref_idx[t]), f"token {t}: top-{k} set differs"
+        else:
+            kth = np.sort(Lref[t])[::-1][k - 1]
+            certain = np.nonzero(Lref[t] > kth + 2 * delta[t])[0]
+            cand = np.nonzero(np.abs(Lref[t] - kth) <= 2 * delta[t])[0]
+            valid = [set(certain) | set(c) for c in
+                     itertools.combinations(cand, k - len(certain))]
+            assert set(idx[t]) in valid, f"token {t}: {sorted(idx[t])} is not a valid top-{k}"
+        # slot order: descending in the kernel's own fp32 scores, ties to the
+        # higher expert index
+        s = L[t, idx[t]]
+        for i in range(k - 1):
+            assert s[i] > s[i + 1] or (s[i] == s[i + 1] and idx[t, i] > idx[t, i + 1])
+    # the grouping counts are the routing histogram
+    np.testing.assert_array_equal(counts, np.bincount(idx.reshape(-1), minlength=fx.E))
+    sel_idx = idx.copy()        # validated above against the oracle's sets
+    # routing weights of the selected sets, from the oracle's logits
+    sel_l = np.take_along_axis(Lref, sel_idx.astype(np.int64), 1)
+    ex = np.exp(sel_l - sel_l.max(axis=1, keepdims=True))
+    wref = ex / ex.sum(axis=1, keepdims=True)
+    d_l = np.take_along_axis(lb, sel_idx.astype(np.int64), 1)
+    dw = wref * (d_l + (wref * d_l).sum(axis=1, keepdims=True)) + 1e-6
+    assert_bounded(w, wref, dw, "routing weights")
+
+    tokens = range(T) if tokens is None else tokens
+    H = fx.H
+    Yref = np.zeros((len(tokens), H))
+    bound = np.zeros((len(tokens), H))
+    for r, t in enumerate(tokens):
+        for i in range(k):
+            e = int(sel_idx[t, i])
+            y, Sd, Pd = oracle.expert_f64(Xc[t], fx.oracle_expert(e))
+            Yref[r] += wref[t, i] * y
+            bound[r] += rel * wref[t, i] * (Sd + Pd) + dw[t, i] * np.abs(y)
+    tok = np.asarray(list(tokens))
+    assert_bounded(Y[tok], Yref, bound, "moe output")
+    if rel > 1e-5:
+        assert_normwise(Y[tok], Yref, rel, "moe output")
+    return idx
+
+
+SMALL = [(8, 256, 128, 4, 64, 2, 1), (8, 256, 128, 4, 64, 2, 5), (16, 128, 192, 8, 64, 4, 33),
+         (4, 384, 128, 8, 128, 1, 17), (32, 512, 256, 4, 128, 6, 40)]
+
+
+@pytest.mark.parametrize("E,H,I,bits,group,k,T", SMALL)
+def test_moe_fp32_small(E, H, I, bits, group, k, T):
+    say(f"moe fp32 E={E} H={H} I={I} bits={bits} group={group} k={k} T={T}")
+    fx = MoeFixture(E, H, I, bits, group, seed=4, bias_std=0.5 if T > 5 else None)
+    X = synth.normal((T, H), 1.0, 4, synth.X, T, device="cuda")
+    check_moe(fx, X, k, dsq.MATH_FP32, 1e-5)
+
+
+@pytest.mark.parametrize("E,H,I,bits,group,k,T", [(8, 256, 128, 8, 128, 2, 64),
+                                                  (16, 512, 256, 4, 64, 4, 100),
+                                                  (8, 128, 192, 8, 64, 3, 7)])
+def test_moe_bf16_small(E, H, I, bits, group, k, T):
+    say(f"moe bf16 E={E} H={H} I={I} bits={bits} group={group} k={k} T={T}")
+    fx = MoeFixture(E, H, I, bits, group, seed=5)
+    X = synth.normal((T, H), 1.0, 5, synth.X, T, device="cuda")
+    check_moe(fx, X, k, dsq.MATH_BF16_MFMA, 1e-2)
+
+
+def test_moe_single_expert_is_dense_swiglu():
+    """E = 1, k = 1: the layer reduces to one dense SwiGLU FFN with weight 1."""
+    say("moe E=1 k=1")
+    fx = MoeFixture(1, 256, 128, 8, 64, seed=6)
+    X = synth.normal((9, 256), 1.0, 6, synth.X, 9, device="cuda")
+    idx = check_moe(fx, X, 1, dsq.MATH_FP32, 1e-5)
+    assert (idx == 0).all()
+
+
+def test_moe_decode_one_token_full_size():
+    """One token, hidden 4096, 256 INT4 group-64 experts (I = 2048), top-6,
+    fp32 router 4096x256."""
+    say("moe decode T=1 full size")
+    fx = MoeFixture(256, 4096, 2048, 4, 64, seed=0)
+    X = synth.normal((1, 4096), 1.0, 0, synth.X, 3, device="cuda")
+    check_moe(fx, X, 6, dsq.MATH_FP32, 1e-5)
+
+
+def test_moe_batched_decode_32_tokens_skewed_full_size():
+    """32 tokens through the same layer shape with a per-expert router bias
+    ~N(0,1) that makes expert load uneven; experts grouped before the GEMMs."""
+    say("moe batched decode T=32 full size, skewed")
+    fx = MoeFixture(256, 4096, 2048, 4, 64, seed=0, bias_std=1.0)
+    X = synth.normal((32, 4096), 1.0, 0, synth.X, 4, device="cuda")
+    idx = check_moe(fx, X, 6, dsq.MATH_FP32, 1e-5)
+    say(f"  distinct experts touched: {len(np.unique(idx))}, "
+        f"max tokens per expert: {np.bincount(idx.reshape(-1)).max()}")
+
+
+def test_moe_prefill_256_tokens_full_size_sampled():
+    """256 tokens, 256 INT8 group-128 SwiGLU experts, bf16 MFMA path; routing
+    of all tokens is checked, the output on 8 sampled tokens."""
+    say("moe prefill T=256 full size INT8 g128 bf16")
+    fx = MoeFixture(256, 4096, 2048, 8, 128, seed=0)
+    X = synth.normal((256, 4096), 1.0, 0, synth.X, 5, device="cuda")
+    check_moe(fx, X, 6, dsq.MATH_BF16_MFMA, 1e-2, tokens=[0, 1, 37, 100, 128, 200, 254, 255])
