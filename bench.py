@@ -97,6 +97,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--cases", default="gemv8,gemv4,moe1,moe32,gemm256,moe256",
+                    help="secondary workloads to run (comma list)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
@@ -186,8 +188,8 @@ def main():
     del W4
     torch.cuda.empty_cache()
 
-    if not args.no_secondary:
-        result["secondary"] = secondary(dsq, synth, torch, np, dev, WV, x, yv)
+    if not args.no_secondary and args.cases:
+        result["secondary"] = secondary(dsq, synth, torch, np, dev, set(args.cases.split(",")), x)
     del WV
     torch.cuda.empty_cache()
 
@@ -196,7 +198,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def secondary(dsq, synth, torch, np, dev, WV, x, yv):
+def secondary(dsq, synth, torch, np, dev, cases, x):
     out = []
     K = 4096
 
@@ -218,8 +220,10 @@ def secondary(dsq, synth, torch, np, dev, WV, x, yv):
                             "so the Infinity Cache cannot hold them"})
         log(out[-1])
 
-    rotated_gemv(8, 64, "INT8 g64 GEMV 4096x4096 (M=1)", 64)
-    rotated_gemv(4, 64, "INT4 g64 GEMV 4096x4096 (M=1)", 64)
+    if "gemv8" in cases:
+        rotated_gemv(8, 64, "INT8 g64 GEMV 4096x4096 (M=1)", 64)
+    if "gemv4" in cases:
+        rotated_gemv(4, 64, "INT4 g64 GEMV 4096x4096 (M=1)", 64)
     torch.cuda.empty_cache()
 
     # MoE decode layers: 256 experts, H=4096, I=2048, top-6
@@ -263,15 +267,30 @@ def secondary(dsq, synth, torch, np, dev, WV, x, yv):
         out.append(rec)
         log(rec)
 
-    r, b, g, u, d = build_moe(4, 64, None)
-    moe_case("MoE decode T=1, 256 experts top-6, INT4 g64 SwiGLU",
-             dsq.MoeLayer(r, g, u, d, None, 6), 1, 64, dsq.MATH_FP32, 4, 64, 64)
-    bias = synth.normal((256,), 1.0, 0, synth.BIAS, 0, device=dev)
-    moe_case("MoE batched decode T=32 skewed (router bias ~N(0,1)), INT4 g64",
-             dsq.MoeLayer(r, g, u, d, bias, 6), 32, 8, dsq.MATH_FP32, 4, 64, 16)
-    del g, u, d
-    torch.cuda.empty_cache()
+    if "moe1" in cases or "moe32" in cases:
+        r, b, g, u, d = build_moe(4, 64, None)
+        if "moe1" in cases:
+            moe_case("MoE decode T=1, 256 experts top-6, INT4 g64 SwiGLU",
+                     dsq.MoeLayer(r, g, u, d, None, 6), 1, 64, dsq.MATH_FP32, 4, 64, 64)
+        if "moe32" in cases:
+            bias = synth.normal((256,), 1.0, 0, synth.BIAS, 0, device=dev)
+            moe_case("MoE batched decode T=32 skewed (router bias ~N(0,1)), INT4 g64",
+                     dsq.MoeLayer(r, g, u, d, bias, 6), 32, 8, dsq.MATH_FP32, 4, 64, 16)
+        del g, u, d
+        torch.cuda.empty_cache()
+    if "gemm256" in cases:
+        out.append(dense_prefill(dsq, synth, torch, dev))
+    if "moe256" in cases:
+        r, b, g, u, d = build_moe(8, 128, None)
+        moe_case("MoE prefill T=256, 256 experts top-6, INT8 g128 SwiGLU, bf16 MFMA",
+                 dsq.MoeLayer(r, g, u, d, None, 6), 256, 1, dsq.MATH_BF16_MFMA, 8, 128, 8)
+        del g, u, d
+        torch.cuda.empty_cache()
+    return out
 
+
+def dense_prefill(dsq, synth, torch, dev):
+    K = 4096
     # dense prefill GEMM M=256, INT8 g128, bf16 MFMA, rotating 32 weight copies
     Ws = []
     for c in range(32):
@@ -292,17 +311,11 @@ def secondary(dsq, synth, torch, np, dev, WV, x, yv):
            "us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
            "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
            "GB/s": round((qbytes(8, 128, K, 4096) + 2 * 256 * K * 4) / (ms * 1e-3) / 1e9, 1)}
-    out.append(rec)
     log(rec)
     del Ws
     torch.cuda.empty_cache()
+    return rec
 
-    r, b, g, u, d = build_moe(8, 128, None)
-    moe_case("MoE prefill T=256, 256 experts top-6, INT8 g128 SwiGLU, bf16 MFMA",
-             dsq.MoeLayer(r, g, u, d, None, 6), 256, 1, dsq.MATH_BF16_MFMA, 8, 128, 8)
-    del g, u, d
-    torch.cuda.empty_cache()
-    return out
 
 
 def cpu_baseline(seconds, np):

@@ -15,6 +15,9 @@ using namespace dsq;
 namespace {
 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
+// Up to this many tokens the fp32 MoE runs each (token, slot) pair as its own
+// GEMV instead of grouping tokens by expert.
+constexpr int64_t kDecodeMaxTokens = 4;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -291,8 +294,24 @@ dsq_status dsq_moe_ffn(const float* X, const float* router_w, const float* bias,
   hipError_t e;
 #define DSQ_TRY(call)                          \
   if ((e = (call)) != hipSuccess) return hip_status(e);
+  if (!bf16 && T <= kDecodeMaxTokens && decode_supported(gate->bits, H, I, E, top_k)) {
+    // Decode: every (token, slot) pair is its own GEMV; no grouping needed.
+    // The gate/up kernel ranks the scores itself and publishes idx/w.
+    DSQ_TRY(launch_router_gemv(X, T, router_w, bias, E, H, m.logits, st));
+    DSQ_TRY(launch_moe_decode(*gate, *up, *down, X, T, E, top_k, m.logits, m.idx, m.w,
+                              static_cast<float*>(m.hbuf), Y, st));
+    if (expert_counts_out) {
+      DSQ_TRY(launch_group(m.idx, T, top_k, E, m.bitmap, m.counts, m.offsets, m.perm, m.pos,
+                           m.active, m.n_active, st));
+    }
+    return DSQ_OK;
+  }
   // (1) router logits, fp32, bias included
-  DSQ_TRY(launch_router(X, T, router_w, bias, E, H, m.logits, st));
+  if (T <= 32) {
+    DSQ_TRY(launch_router_gemv(X, T, router_w, bias, E, H, m.logits, st));
+  } else {
+    DSQ_TRY(launch_router(X, T, router_w, bias, E, H, m.logits, st));
+  }
   // (2) softmax + top-k + renormalisation
   DSQ_TRY(launch_topk(m.logits, nullptr, T, E, top_k, m.idx, m.w, st));
   // (3) stable grouping by expert

@@ -152,4 +152,55 @@ __device__ __forceinline__ uint2 ld_nt(const uint2* p) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// ---------------------------------------------------------------------------
+// Activation vectors staged in LDS.  A lane reads its 16-byte chunk's
+// EPC = 16 or 32 floats (F = EPC / 4 float4 slots) as F ds_read_b128 at a
+// stride of F slots between lanes; rotating each chunk's slots by its chunk
+// index spreads the lanes of one read over distinct banks.
+// ---------------------------------------------------------------------------
+template <int F>
+__device__ __forceinline__ int lds_slot(int f) {
+  const int c = f / F, j = f % F;
+  return c * F + ((j + (F == 4 ? (c >> 1) : c)) & (F - 1));
+}
+
+// All threads of the workgroup copy n floats (n % 4 == 0) into LDS, swizzled
+// for chunks of F float4.  The caller synchronises afterwards.
+template <int F>
+__device__ __forceinline__ void stage_lds(const float* __restrict__ src, int n, float4* lds) {
+  const float4* s4 = reinterpret_cast<const float4*>(src);
+  for (int f = threadIdx.x; f < n / 4; f += blockDim.x) lds[lds_slot<F>(f)] = s4[f];
+}
+
+// ---------------------------------------------------------------------------
+// Wave-wide argmax by (value desc, index desc) with DPP row shifts and row
+// broadcasts; every lane returns the winner.  Lanes with index < 0 hold no
+// candidate.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia > ib);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(
+      __float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
+  const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xf, false);
+  if (oi >= 0 && (i < 0 || ranks_before(ov, oi, v, i))) {
+    v = ov;
+    i = oi;
+  }
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  argmax_step<0x111, 0xf>(v, i);  // row_shr:1
+  argmax_step<0x112, 0xf>(v, i);  // row_shr:2
+  argmax_step<0x114, 0xf>(v, i);  // row_shr:4
+  argmax_step<0x118, 0xf>(v, i);  // row_shr:8   -> lane 15 of each row
+  argmax_step<0x142, 0xa>(v, i);  // row_bcast:15 into rows 1 and 3
+  argmax_step<0x143, 0xc>(v, i);  // row_bcast:31 into rows 2 and 3 -> lane 63
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
+
 }  // namespace dsq

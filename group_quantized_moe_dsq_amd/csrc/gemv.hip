@@ -16,12 +16,25 @@
 //     factored per chunk:  sum_c x*(q - zp)*s = s * (sum_c x*q - zp * sum_c x)
 //     with sum_c x precomputed per lane.  Per code that leaves one convert and
 //     one FMA.
-//   * R rows are in flight per wave; their partial sums are reduced across the
-//     wave in one reduce-scatter, after which R lanes store the R outputs.
+//   * R rows per wave step; their partial sums are reduced across the wave in
+//     one reduce-scatter, after which R lanes store the R outputs.  The next
+//     step's loads are issued before the current step's arithmetic.
 #include "common.h"
+#include "gemv_core.h"
 #include "internal.h"
 
 namespace dsq {
+
+// Launch shape (tuned on MI355X; overridable at build time for sweeps).
+#ifndef DSQ_GEMV_R8
+#define DSQ_GEMV_R8 2  // rows per wave step, INT8
+#endif
+#ifndef DSQ_GEMV_R4
+#define DSQ_GEMV_R4 4  // rows per wave step, INT4
+#endif
+#ifndef DSQ_GEMV_WAVES_PER_CU
+#define DSQ_GEMV_WAVES_PER_CU 8
+#endif
 
 template <int BITS, int R, int KCH>
 __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ payload,
@@ -29,7 +42,6 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ p
                                                    const float* __restrict__ x,
                                                    float* __restrict__ y, int N, int K,
                                                    int group) {
-  constexpr int EPC = Codes<BITS>::kPerChunk;  // codes per 16-byte chunk
   const int lane = threadIdx.x & 63;
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int nwaves = (gridDim.x * blockDim.x) >> 6;
@@ -37,77 +49,50 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ p
   const int nchunk = row_bytes / 16;
   const int groups = K / group;
 
-  // This lane's slice of x: chunk i covers x[(lane + 64 i) * EPC ...].
-  float xr[KCH][EPC];
-  float xs[KCH];
-#pragma unroll
-  for (int i = 0; i < KCH; ++i) {
-    const int c = lane + 64 * i;
-    xs[i] = 0.0f;
-    if (c < nchunk) {
-      const float4* x4 = reinterpret_cast<const float4*>(x + c * EPC);
-#pragma unroll
-      for (int j = 0; j < EPC / 4; ++j) {
-        const float4 v = x4[j];
-        xr[i][4 * j + 0] = v.x;
-        xr[i][4 * j + 1] = v.y;
-        xr[i][4 * j + 2] = v.z;
-        xr[i][4 * j + 3] = v.w;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) xr[i][e] = 0.0f;
-    }
-    float s = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) s += xr[i][e];
-    xs[i] = s;
-  }
-
-  for (int rb = wave; rb * R < N; rb += nwaves) {
-    uint4 w[R][KCH];
-    float2 m[R][KCH];
+  auto load = [&](RowChunks<BITS, R, KCH>& C, int rb) {
+    const uint8_t* prow[R];
+    const float2* mrow[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int row = min(rb * R + r, N - 1);
-      const uint4* prow = reinterpret_cast<const uint4*>(payload + int64_t(row) * row_bytes);
-      const float2* mrow = meta + int64_t(row) * groups;
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        const int c = lane + 64 * i;
-        if (c < nchunk) {
-          w[r][i] = ld_nt(prow + c);
-          m[r][i] = mrow[(c * EPC) / group];
-        } else {
-          w[r][i] = make_uint4(0, 0, 0, 0);
-          m[r][i] = make_float2(0.0f, 0.0f);
-        }
-      }
+      prow[r] = payload + int64_t(row) * row_bytes;
+      mrow[r] = meta + int64_t(row) * groups;
     }
+    C.load(prow, mrow, nchunk, group, lane);
+  };
+  XSlice<BITS, KCH> xs;  // this lane's slice of x, reused for every row
+  auto finish = [&](const RowChunks<BITS, R, KCH>& C, int rb) {
     float acc[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      acc[r] = 0.0f;
-#pragma unroll
-      for (int i = 0; i < KCH; ++i) {
-        float f[EPC];
-        Codes<BITS>::unpack(w[r][i], f);
-        // two interleaved chains for ILP
-        float d0 = 0.0f, d1 = 0.0f;
-#pragma unroll
-        for (int e = 0; e < EPC; e += 2) {
-          d0 = fmaf(xr[i][e], f[e], d0);
-          d1 = fmaf(xr[i][e + 1], f[e + 1], d1);
-        }
-        const float d = d0 + d1;
-        acc[r] = fmaf(m[r][i].x, fmaf(-m[r][i].y, xs[i], d), acc[r]);
-      }
-    }
+    C.dot(xs, acc);
     const float tot = wave_reduce_scatter<R>(acc);
     if ((lane & (64 / R - 1)) == 0) {
       const int row = rb * R + reduce_scatter_row<R>(lane);
       if (row < N) y[row] = tot;
     }
+  };
+
+  // Two buffers: the loads of the wave's next row block are in flight while
+  // the current one is dequantized and reduced.  The first weight loads are
+  // issued before x is staged, so the two latencies overlap; x is read from
+  // memory once per workgroup and shared through LDS.
+  extern __shared__ float4 xl[];
+  RowChunks<BITS, R, KCH> A, B;
+  int rb = wave;
+  if (rb * R < N) load(A, rb);
+  stage_lds<Codes<BITS>::kPerChunk / 4>(x, K, xl);
+  __syncthreads();
+  xs.load_lds(xl, nchunk, lane);
+  xs.sums();
+  while (rb * R < N) {
+    const int rb1 = rb + nwaves;
+    const bool more1 = rb1 * R < N;
+    if (more1) load(B, rb1);
+    finish(A, rb);
+    if (!more1) break;
+    const int rb2 = rb1 + nwaves;
+    if (rb2 * R < N) load(A, rb2);
+    finish(B, rb1);
+    rb = rb2;
   }
 }
 
@@ -167,7 +152,7 @@ __global__ __launch_bounds__(256) void gemv_kernel_long(const uint8_t* __restric
 
 namespace {
 
-constexpr int kMaxWaves = 256 * 8;  // 8 waves per CU at most, grid-stride beyond
+constexpr int kMaxWaves = 256 * DSQ_GEMV_WAVES_PER_CU;  // grid-stride beyond
 
 template <int BITS, int R, int KCH>
 hipError_t go(const QMat& q, const float* x, float* y, int N, int K, int group,
@@ -175,8 +160,8 @@ hipError_t go(const QMat& q, const float* x, float* y, int N, int K, int group,
   const int rowblocks = (N + R - 1) / R;
   const int waves = rowblocks < kMaxWaves ? rowblocks : kMaxWaves;
   const int blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((gemv_kernel<BITS, R, KCH>), dim3(blocks), dim3(256), 0, stream, q.payload,
-                     q.meta, x, y, N, K, group);
+  hipLaunchKernelGGL((gemv_kernel<BITS, R, KCH>), dim3(blocks), dim3(256), size_t(K) * 4, stream,
+                     q.payload, q.meta, x, y, N, K, group);
   return hipGetLastError();
 }
 
@@ -196,11 +181,12 @@ hipError_t dispatch(const QMat& q, const float* x, float* y, int N, int K, int g
                     hipStream_t stream) {
   const int nchunk = K * BITS / 8 / 16;
   const int kch = (nchunk + 63) / 64;
+  constexpr int R = BITS == 8 ? DSQ_GEMV_R8 : DSQ_GEMV_R4;
   switch (kch) {
-    case 1: return go<BITS, 4, 1>(q, x, y, N, K, group, stream);
-    case 2: return go<BITS, 4, 2>(q, x, y, N, K, group, stream);
-    case 3: return go<BITS, 4, 3>(q, x, y, N, K, group, stream);
-    case 4: return go<BITS, 4, 4>(q, x, y, N, K, group, stream);
+    case 1: return go<BITS, R, 1>(q, x, y, N, K, group, stream);
+    case 2: return go<BITS, R, 2>(q, x, y, N, K, group, stream);
+    case 3: return go<BITS, R, 3>(q, x, y, N, K, group, stream);
+    case 4: return go<BITS, R, 4>(q, x, y, N, K, group, stream);
     default: return go_long<BITS, 4>(q, x, y, N, K, group, stream);
   }
 }

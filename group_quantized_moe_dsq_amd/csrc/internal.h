@@ -53,6 +53,18 @@ hipError_t launch_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, uin
 hipError_t launch_combine(const float* ybuf, const int32_t* pos, const float* w, int64_t T,
                           int32_t k, int64_t H, float* Y, hipStream_t stream);
 
+// Decode path (few tokens): fp32 router GEMV, and the expert FFN per routing
+// slot (gate/up GEMV + SwiGLU into hbuf [T*k][I], then down GEMV fused with
+// the weighted combine into Y).
+hipError_t launch_router_gemv(const float* X, int64_t T, const float* Wr, const float* bias,
+                              int32_t E, int64_t H, float* logits, hipStream_t stream);
+bool decode_supported(int bits, int64_t H, int64_t I, int32_t E, int32_t k);
+// Ranks each token's scores itself (writing idx/w), so no separate top-k.
+hipError_t launch_moe_decode(const dsq_qweight& gate, const dsq_qweight& up,
+                             const dsq_qweight& down, const float* X, int64_t T, int32_t E,
+                             int32_t k, const float* logits, int32_t* idx, float* w, float* hbuf,
+                             float* Y, hipStream_t stream);
+
 // bf16 MFMA path
 hipError_t launch_to_bf16(const float* X, int64_t n, uint16_t* out, hipStream_t stream);
 

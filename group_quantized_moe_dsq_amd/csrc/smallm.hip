@@ -290,15 +290,11 @@ hipError_t launch_router(const float* X, int64_t T, const float* Wr, const float
 // Softmax + top-k + renormalisation ("Hand-writing a DeepSeek inference
 // engine in pure C" §3.4: subtract the maximum; §3.5: top-k by a greater-first
 // sort of (score, index) pairs).  One wave per token; each lane holds EPL
-// scores.  k rounds of a wave-wide argmax with the comparator
+// scores.  k rounds of a wave-wide DPP argmax with the comparator
 // (score desc, index desc); lane i keeps the i-th winner.  The renormalised
 // weight of a selected expert is exp(s_i - s_max) / sum_sel exp(s_j - s_max):
 // the full softmax denominator cancels in p_i / sum_sel p_j.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia > ib);
-}
-
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
                                                    const float* __restrict__ bias, int T, int E,
@@ -309,18 +305,20 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   if (t >= T) return;
   float v[EPL];
   uint64_t taken = 0;
+  // all loads first (clamped addresses, no branches), then the fix-ups
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) v[j] = logits[int64_t(t) * E + min(lane + 64 * j, E - 1)];
+  if (bias) {
+    float b[EPL];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) b[j] = bias[min(lane + 64 * j, E - 1)];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) v[j] += b[j];
+  }
 #pragma unroll
   for (int j = 0; j < EPL; ++j) {
-    const int e = lane + 64 * j;
-    float s = -INFINITY;
-    if (e < E) {
-      s = logits[int64_t(t) * E + e];
-      if (bias) s += bias[e];
-      if (s != s) s = -INFINITY;  // NaN ranks last
-    } else {
-      taken |= uint64_t(1) << j;  // padding never wins
-    }
-    v[j] = s;
+    if (v[j] != v[j]) v[j] = -INFINITY;  // NaN ranks last
+    if (lane + 64 * j >= E) taken |= uint64_t(1) << j;  // padding never wins
   }
   float my_val = 0.0f;
   int my_idx = 0;
@@ -337,16 +335,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
         bi = e;
       }
     }
-    // wave argmax; lanes without a candidate carry index -1
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (oi >= 0 && (bi < 0 || ranks_before(ov, oi, bv, bi))) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    wave_argmax(bv, bi);  // DPP reduction; uniform across the wave
     if (bi >= 0 && (bi & 63) == lane) taken |= uint64_t(1) << (bi >> 6);
     if (i == 0) best_val = bv;
     if (lane == i) {
