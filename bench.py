@@ -301,7 +301,7 @@ def dense_prefill(dsq, synth, torch, dev):
     del w
     X = synth.normal((256, K), 1.0, 0, synth.X, 5, device=dev)
     Y = torch.empty((256, 4096), device=dev)
-    wsb = torch.empty(dsq.gemm_workspace_bytes(256, K, dsq.MATH_BF16_MFMA) + 256,
+    wsb = torch.empty(dsq.gemm_workspace_bytes(256, 4096, K, dsq.MATH_BF16_MFMA) + 256,
                       dtype=torch.uint8, device=dev)
     ms = time_calls(lambda i: dsq.gemm(Ws[i % 32], X, Y, math=dsq.MATH_BF16_MFMA, workspace=wsb),
                     128, 16, torch)

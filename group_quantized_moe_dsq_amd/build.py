@@ -11,7 +11,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsq.so")
-SOURCES = ["api.hip", "pack.hip", "gemv.hip", "decode.hip", "smallm.hip", "mfma.hip"]
+SOURCES = ["api.hip", "pack.hip", "gemv.hip", "decode.hip", "smallm.hip", "mfma.hip",
+           "gemm_mfma.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -186,12 +186,12 @@ dsq_status dsq_gemv(const dsq_qweight* W, int64_t expert, const float* x, float*
   return hip_status(launch_gemv(*W, expert, x, y, (hipStream_t)stream));
 }
 
-size_t dsq_gemm_workspace_bytes(int64_t M, int64_t K, int32_t math) {
-  if (M < 0 || K <= 0) return 0;
+size_t dsq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t math) {
+  if (M < 0 || N <= 0 || K <= 0) return 0;
   if (math != DSQ_MATH_FP32 && math != DSQ_MATH_BF16_MFMA && math != DSQ_MATH_AUTO) return 0;
   if (!use_bf16(math, M)) return 0;
-  if (!mul_ok(M, K)) return 0;
-  return size_t(align256(M * K * 2));
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim || !mul_ok(M, K) || !mul_ok(M, N)) return 0;
+  return gemm_mfma_workspace(M, N, K);
 }
 
 dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float* Y, int64_t M,
@@ -207,7 +207,7 @@ dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float*
   if (!aligned(X, 16) || !aligned(Y, 4)) return DSQ_ERR_ALIGN;
   const bool bf16 = use_bf16(math, M);
   if (bf16) {
-    const size_t need = dsq_gemm_workspace_bytes(M, W->K, math);
+    const size_t need = dsq_gemm_workspace_bytes(M, W->N, W->K, math);
     if (!workspace || workspace_bytes < need) return DSQ_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return DSQ_ERR_ALIGN;
   }
@@ -219,10 +219,7 @@ dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float*
     return hip_status(
         launch_smallm_f32(*W, nullptr, expert, nullptr, XR_DENSE, X, M, Y, W->N, st));
   }
-  uint16_t* xb = static_cast<uint16_t*>(workspace);
-  hipError_t e = launch_to_bf16(X, M * W->K, xb, st);
-  if (e != hipSuccess) return hip_status(e);
-  return hip_status(launch_mfma_gemm(*W, nullptr, expert, nullptr, XR_DENSE, xb, M, Y, 0, W->N, st));
+  return hip_status(launch_gemm_mfma(*W, expert, X, Y, M, workspace, st));
 }
 
 dsq_status dsq_moe_route_topk(const float* logits, const float* bias, int64_t T, int32_t E,

@@ -64,7 +64,7 @@ def lib():
         L.dsq_pack_weights.restype = i32
         L.dsq_gemv.argtypes = [pd, i64, vp, vp, vp]
         L.dsq_gemv.restype = i32
-        L.dsq_gemm_workspace_bytes.argtypes = [i64, i64, i32]
+        L.dsq_gemm_workspace_bytes.argtypes = [i64, i64, i64, i32]
         L.dsq_gemm_workspace_bytes.restype = sz
         L.dsq_gemm.argtypes = [pd, i64, vp, vp, i64, i32, vp, sz, vp]
         L.dsq_gemm.restype = i32
@@ -154,8 +154,8 @@ def gemv(W: QWeight, x: torch.Tensor, y: torch.Tensor | None = None, expert: int
     return y
 
 
-def gemm_workspace_bytes(M: int, K: int, math: int) -> int:
-    return int(lib().dsq_gemm_workspace_bytes(M, K, math))
+def gemm_workspace_bytes(M: int, N: int, K: int, math: int) -> int:
+    return int(lib().dsq_gemm_workspace_bytes(M, N, K, math))
 
 
 def gemm(W: QWeight, X: torch.Tensor, Y: torch.Tensor | None = None, expert: int = 0,
@@ -164,7 +164,7 @@ def gemm(W: QWeight, X: torch.Tensor, Y: torch.Tensor | None = None, expert: int
     M = X.shape[0]
     if Y is None:
         Y = torch.empty((M, W.N), dtype=torch.float32, device=X.device)
-    need = gemm_workspace_bytes(M, W.K, math)
+    need = gemm_workspace_bytes(M, W.N, W.K, math)
     if workspace is None and need:
         workspace = torch.empty(need + 256, dtype=torch.uint8, device=X.device)
     wptr, wbytes = None, 0

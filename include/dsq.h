@@ -151,13 +151,16 @@ dsq_status dsq_gemv(const dsq_qweight* W, int64_t expert, const float* x, float*
  * decode and prefill).
  *   X : fp32 [M][K] device.   Y : fp32 [M][N] device (written).
  *   math : DSQ_MATH_FP32, DSQ_MATH_BF16_MFMA or DSQ_MATH_AUTO.
- *   workspace : device scratch of dsq_gemm_workspace_bytes(M, K, math)
- *               bytes (may be NULL when that is 0), 256-byte aligned.
+ *   workspace : device scratch of dsq_gemm_workspace_bytes(M, N, K, math)
+ *               bytes (may be NULL when that is 0), 256-byte aligned; its
+ *               contents on entry are ignored.  It holds X in bf16 and, when
+ *               the bf16 path splits K across workgroups, the fp32 partial
+ *               tiles, which are added in a fixed order (deterministic).
  * FP32: |err| <= 1e-5 * sum|x w| per output.  BF16_MFMA: X and the
  * dequantized weights are rounded to bf16 and products are summed in fp32:
  * |err| <= 1e-2 * sum|x w| per output.
  */
-size_t dsq_gemm_workspace_bytes(int64_t M, int64_t K, int32_t math);
+size_t dsq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t math);
 dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float* Y, int64_t M,
                     int32_t math, void* workspace, size_t workspace_bytes, void* stream);
 
