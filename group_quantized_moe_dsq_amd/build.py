@@ -11,8 +11,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsq.so")
-SOURCES = ["api.hip", "pack.hip", "gemv.hip", "decode.hip", "smallm.hip", "mfma.hip",
-           "gemm_mfma.hip"]
+SOURCES = ["api.hip", "pack.hip", "gemv.hip", "decode.hip", "route.hip",
+           "gemm_mfma.hip",
+           "gmm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -92,11 +92,14 @@ struct MoeWs {
   uint32_t* bitmap;
   void* hbuf;
   float* ybuf;
-  uint16_t* xb;
+  void* act;         // activations of the token tiles in MFMA operand order
+  size_t act_bytes;
+  float* xs;         // their per-group sums
+  size_t xs_bytes;
 };
 
-int64_t moe_layout(void* ws, int64_t T, int32_t E, int32_t k, int64_t H, int64_t I, bool bf16,
-                   MoeWs* out, bool* overflow) {
+int64_t moe_layout(void* ws, int64_t T, int32_t E, int32_t k, int64_t H, int64_t I, int group,
+                   bool bf16, MoeWs* out, bool* overflow) {
   Carver c(ws);
   MoeWs m{};
   const int64_t nk = T * k;
@@ -110,9 +113,18 @@ int64_t moe_layout(void* ws, int64_t T, int32_t E, int32_t k, int64_t H, int64_t
   m.active = static_cast<int32_t*>(c.take(E, 4));
   m.n_active = static_cast<int32_t*>(c.take(1, 4));
   m.bitmap = static_cast<uint32_t*>(c.take(int64_t(E) * ((T + 31) / 32), 4));
-  m.hbuf = c.take(nk * I, bf16 ? 2 : 4);
+  m.hbuf = c.take(nk * I, 4);
   m.ybuf = static_cast<float*>(c.take(nk * H, 4));
-  m.xb = bf16 ? static_cast<uint16_t*>(c.take(T * H, 2)) : nullptr;
+  // token tiles of the grouped GEMM: routed rows nk in at most min(nk, E) experts
+  const int xp = bf16 ? 1 : 2;
+  const int64_t kmax = H > I ? H : I;
+  const int64_t segs = nk < E ? nk : E;
+  m.act_bytes = gmm_act_bytes(nk, segs, xp, kmax);
+  m.act = c.take(int64_t(m.act_bytes), 1);
+  m.xs_bytes = gmm_xs_bytes(nk, segs, xp, kmax, group);
+  m.xs = static_cast<float*>(c.take(int64_t(m.xs_bytes), 1));
+  // the grouped GEMM addresses these with 32-bit offsets
+  if (m.act_bytes > size_t(INT32_MAX) || m.xs_bytes > size_t(INT32_MAX)) c.overflow = true;
   if (out) *out = m;
   if (overflow) *overflow = c.overflow;
   return c.used;
@@ -189,9 +201,14 @@ dsq_status dsq_gemv(const dsq_qweight* W, int64_t expert, const float* x, float*
 size_t dsq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t math) {
   if (M < 0 || N <= 0 || K <= 0) return 0;
   if (math != DSQ_MATH_FP32 && math != DSQ_MATH_BF16_MFMA && math != DSQ_MATH_AUTO) return 0;
-  if (!use_bf16(math, M)) return 0;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim || !mul_ok(M, K) || !mul_ok(M, N)) return 0;
-  return gemm_mfma_workspace(M, N, K);
+  if (use_bf16(math, M)) return gemm_mfma_workspace(M, N, K);
+  if (M < 2) return 0;  // GEMV
+  // fp32 path: the token tiles of the grouped GEMM (one segment), sized for
+  // the smallest supported group
+  const size_t a = gmm_act_bytes(M, 1, 2, K), x = gmm_xs_bytes(M, 1, 2, K, 64);
+  if (a > size_t(INT32_MAX) || x > size_t(INT32_MAX)) return 0;
+  return a + x;
 }
 
 dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float* Y, int64_t M,
@@ -206,20 +223,22 @@ dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float*
   if (M > kMaxDim || !mul_ok(M, W->K) || !mul_ok(M, W->N)) return DSQ_ERR_OVERFLOW;
   if (!aligned(X, 16) || !aligned(Y, 4)) return DSQ_ERR_ALIGN;
   const bool bf16 = use_bf16(math, M);
-  if (bf16) {
+  if (M >= 2) {
     const size_t need = dsq_gemm_workspace_bytes(M, W->N, W->K, math);
+    if (need == 0) return DSQ_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < need) return DSQ_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return DSQ_ERR_ALIGN;
   }
   if (M == 0) return DSQ_OK;
   if ((s = check_device()) != DSQ_OK) return s;
   hipStream_t st = (hipStream_t)stream;
-  if (!bf16) {
-    if (M == 1) return hip_status(launch_gemv(*W, expert, X, Y, st));
-    return hip_status(
-        launch_smallm_f32(*W, nullptr, expert, nullptr, XR_DENSE, X, M, Y, W->N, st));
-  }
-  return hip_status(launch_gemm_mfma(*W, expert, X, Y, M, workspace, st));
+  if (bf16) return hip_status(launch_gemm_mfma(*W, expert, X, Y, M, workspace, st));
+  if (M == 1) return hip_status(launch_gemv(*W, expert, X, Y, st));
+  const size_t act = gmm_act_bytes(M, 1, 2, W->K);
+  const size_t xsb = gmm_xs_bytes(M, 1, 2, W->K, 64);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  return hip_status(launch_gmm(*W, nullptr, expert, nullptr, XR_DENSE, X, W->K, M, 2, ws, act,
+                               reinterpret_cast<float*>(ws + act), xsb, Y, W->N, st));
 }
 
 dsq_status dsq_moe_route_topk(const float* logits, const float* bias, int64_t T, int32_t E,
@@ -242,7 +261,9 @@ size_t dsq_moe_workspace_bytes(int64_t T, int32_t E, int32_t top_k, int64_t H, i
   if (math != DSQ_MATH_FP32 && math != DSQ_MATH_BF16_MFMA && math != DSQ_MATH_AUTO) return 0;
   if (T > 65536 || E > 4096 || top_k > 32 || H > kMaxDim || I > kMaxDim) return 0;
   bool ovf = false;
-  const int64_t n = moe_layout(nullptr, T, E, top_k, H, I, use_bf16(math, T), nullptr, &ovf);
+  // the group size enters only the size of the per-group sums: size for the
+  // smallest supported group
+  const int64_t n = moe_layout(nullptr, T, E, top_k, H, I, 64, use_bf16(math, T), nullptr, &ovf);
   return ovf ? 0 : size_t(n);
 }
 
@@ -282,7 +303,7 @@ dsq_status dsq_moe_ffn(const float* X, const float* router_w, const float* bias,
   if ((s = check_device()) != DSQ_OK) return s;
 
   MoeWs m{};
-  moe_layout(workspace, T, E, top_k, H, I, bf16, &m, nullptr);
+  moe_layout(workspace, T, E, top_k, H, I, 64, bf16, &m, nullptr);
   if (logits_out) m.logits = logits_out;
   if (idx_out) m.idx = idx_out;
   if (w_out) m.w = w_out;
@@ -323,17 +344,12 @@ dsq_status dsq_moe_ffn(const float* X, const float* router_w, const float* bias,
   const int64_t max_items = T * top_k < E64 ? T * top_k : E64;
   g.max_items = int32_t(max_items);
   // (4) expert FFNs over their token groups, (5) weighted combine
-  if (bf16) {
-    DSQ_TRY(launch_to_bf16(X, T * H, m.xb, st));
-    DSQ_TRY(launch_mfma_gemm(*gate, up, 0, &g, XR_GATHER, m.xb, 0, m.hbuf, 1, I, st));
-    DSQ_TRY(launch_mfma_gemm(*down, nullptr, 0, &g, XR_SEGMENT,
-                             static_cast<const uint16_t*>(m.hbuf), 0, m.ybuf, 0, H, st));
-  } else {
-    DSQ_TRY(launch_smallm_f32(*gate, up, 0, &g, XR_GATHER, X, 0, static_cast<float*>(m.hbuf), I,
-                              st));
-    DSQ_TRY(launch_smallm_f32(*down, nullptr, 0, &g, XR_SEGMENT, static_cast<float*>(m.hbuf), 0,
-                              m.ybuf, H, st));
-  }
+  const int xp = bf16 ? 1 : 2;
+  float* hbuf = static_cast<float*>(m.hbuf);
+  DSQ_TRY(launch_gmm(*gate, up, 0, &g, XR_GATHER, X, H, 0, xp, m.act, m.act_bytes, m.xs,
+                     m.xs_bytes, hbuf, I, st));
+  DSQ_TRY(launch_gmm(*down, nullptr, 0, &g, XR_SEGMENT, hbuf, I, 0, xp, m.act, m.act_bytes, m.xs,
+                     m.xs_bytes, m.ybuf, H, st));
   DSQ_TRY(launch_combine(m.ybuf, m.pos, m.w, T, top_k, H, Y, st));
 #undef DSQ_TRY
   return DSQ_OK;

@@ -26,16 +26,9 @@ struct Groups {
   int32_t max_items;        // grid bound on the number of active experts
 };
 
-// fp32 grouped small-M kernels.
-//  mode STORE : out[row(m)][n] = sum_k x_m[k] W[n][k]
-//  mode SWIGLU: out[row(m)][n] = silu(x_m Wg[n]) * (x_m Wu[n])
-// x rows: dense -> X + m*K ; moe gather -> X + (perm[p]/top_k)*K ;
-//         moe segment -> X + p*K.   out rows: dense -> m ; moe -> p.
+// Where the rows of a grouped GEMM come from:
+//  dense -> X + m*K ; moe gather -> X + (perm[p]/top_k)*K ; moe segment -> X + p*K.
 enum XRows { XR_DENSE = 0, XR_GATHER = 1, XR_SEGMENT = 2 };
-
-hipError_t launch_smallm_f32(const dsq_qweight& A, const dsq_qweight* B, int64_t expert,
-                             const Groups* grp, int xrows, const float* X, int64_t M,
-                             float* out, int64_t ld_out, hipStream_t stream);
 
 // fp32 router: logits[t][e] = X[t] . Wr[e] (+ bias[e])
 hipError_t launch_router(const float* X, int64_t T, const float* Wr, const float* bias,
@@ -71,11 +64,18 @@ size_t gemm_mfma_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_mfma(const dsq_qweight& W, int64_t expert, const float* X, float* Y,
                             int64_t M, void* workspace, hipStream_t stream);
 
-// bf16 MFMA grouped path
-hipError_t launch_to_bf16(const float* X, int64_t n, uint16_t* out, hipStream_t stream);
-
-hipError_t launch_mfma_gemm(const dsq_qweight& A, const dsq_qweight* B, int64_t expert,
-                            const Groups* grp, int xrows, const uint16_t* Xb, int64_t M,
-                            void* out, int out_bf16, int64_t ld_out, hipStream_t stream);
+// Grouped fused-dequant GEMM on bf16 MFMA (tokens grouped by expert, or one
+// dense matrix).  xp = 2: activations split into two bf16 parts (fp32-accurate
+// results); xp = 1: activations rounded to bf16.  The prep step writes the
+// activations of every token tile into `act`/`xs` (sizes from gmm_act_bytes /
+// gmm_xs_bytes for `rows` routed rows in at most `segments` experts).
+// out rows: dense -> m ; grouped -> p (perm order).  With B (SwiGLU up) the
+// output is silu(x A^T) * (x B^T).
+size_t gmm_act_bytes(int64_t rows, int64_t segments, int xp, int64_t K);
+size_t gmm_xs_bytes(int64_t rows, int64_t segments, int xp, int64_t K, int group);
+hipError_t launch_gmm(const dsq_qweight& A, const dsq_qweight* B, int64_t expert,
+                      const Groups* grp, int xrows, const float* X, int64_t ld_x, int64_t M,
+                      int xp, void* act, size_t act_bytes, float* xs, size_t xs_bytes,
+                      float* out, int64_t ld_out, hipStream_t stream);
 
 }  // namespace dsq

@@ -1,145 +1,63 @@
-// smallm.hip -- fp32 fused-dequant GEMM for few activation rows, dense or
-// grouped by expert, plus the fp32 router.
+// route.hip -- the routing steps of the MoE layer: router logits (fp32
+// weights, few token rows), softmax + top-k + renormalisation, stable
+// grouping of the routed entries by expert, and the weighted combine.
 //
 // Method: "Hand-writing a DeepSeek inference engine in pure C"
-// (hnwysp.cn/news/134870) §3.2 (dequantize inside the matmul loop), §3.3
-// (the matmul), §3.5 (an expert runs once over all tokens routed to it, so
-// its weights are read once per layer; the SwiGLU expert form is the
-// workload's definition).
-//
-// Mapping: a workgroup of 4 waves owns 4*R output rows of one matrix (one
-// expert) and loops over the tokens of that expert in tiles of MT.  K is
-// walked in rounds of 1024: the round's activations of the MT tokens are
-// staged in LDS, and each lane dequantizes 16 consecutive weights of each of
-// its rows once ((q - zp) * scale, fp32) and reuses them for all MT tokens.
-// Partial sums are reduced across the wave in one reduce-scatter.
+// (hnwysp.cn/news/134870) §3.4 (softmax with the maximum subtracted), §3.5
+// (router = a linear layer, top-k by a greater-first sort of (score, index)
+// pairs, tokens gathered per expert, weighted sum of the expert outputs).
 #include "common.h"
 #include "internal.h"
 
 namespace dsq {
 
-// 16 consecutive weights of one row, as floats.
-//  BITS 8 : 16 codes, one 16-byte load
-//  BITS 4 : 16 codes, one 8-byte load (two words of layout version 1)
-//  BITS 32: 16 fp32 weights (unquantized router), four 16-byte loads
-template <int BITS>
-__device__ __forceinline__ void load16(const uint8_t* row, const float2* mrow, int chunk,
-                                       int group, float* f) {
-  if constexpr (BITS == 32) {
-    const float4* p = reinterpret_cast<const float4*>(row) + chunk * 4;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 v = p[j];
-      f[4 * j] = v.x;
-      f[4 * j + 1] = v.y;
-      f[4 * j + 2] = v.z;
-      f[4 * j + 3] = v.w;
-    }
-  } else {
-    const float2 m = mrow[(chunk * 16) / group];
-    if constexpr (BITS == 8) {
-      const uint4 c = ld_nt(reinterpret_cast<const uint4*>(row) + chunk);
-      Codes<8>::unpack(c, f);
-    } else {
-      const uint2 c = ld_nt(reinterpret_cast<const uint2*>(row) + chunk);
-      bytes4_to_float(c.x & 0x0F0F0F0Fu, f + 0);
-      bytes4_to_float((c.x >> 4) & 0x0F0F0F0Fu, f + 4);
-      bytes4_to_float(c.y & 0x0F0F0F0Fu, f + 8);
-      bytes4_to_float((c.y >> 4) & 0x0F0F0F0Fu, f + 12);
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) f[e] = (f[e] - m.y) * m.x;  // exact q - zp, one rounding
-  }
-}
-
-struct SmArgs {
-  const uint8_t* a;        // matrix A of entry 0 (payload)
-  const uint8_t* b;        // matrix B (SwiGLU up) or NULL
-  int64_t stride;          // bytes per batch entry
-  int64_t meta_off;        // offset of (scale, zp) inside an entry
-  int N, K, group;
-  int64_t expert;          // dense mode: batch entry
-  const int32_t* active;   // moe mode
-  const int32_t* n_active;
-  const int32_t* offsets;
-  const int32_t* perm;
-  int top_k;
-  int xrows;
-  const float* X;
-  int64_t M;               // dense mode: number of rows
-  float* out;
-  int64_t ld_out;
-  const float* bias;       // router bias or NULL
+// ---------------------------------------------------------------------------
+// Router logits for many tokens: logits[t][e] = X[t] . Wr[e] (+ bias[e]),
+// fp32 weights.  A workgroup of 4 waves owns 4*R experts and loops over the
+// tokens in tiles of MT.  K is walked in rounds of 1024: the round's
+// activations of the MT tokens are staged in LDS, each lane loads 16
+// consecutive weights of each of its rows once and reuses them for all MT
+// tokens; partial sums are reduced across the wave in one reduce-scatter.
+// (Few tokens take the router GEMV of decode.hip instead.)
+// ---------------------------------------------------------------------------
+struct RouterArgs {
+  const float* W;   // [E][K]
+  int N, K;         // N = E
+  const float* X;   // [M][K]
+  int64_t M;
+  float* out;       // [M][N]
+  const float* bias;
 };
 
 constexpr int kRound = 1024;  // K per LDS round: 64 lanes x 16
 
-template <int BITS, int R, int MT, bool SWIGLU>
-__global__ __launch_bounds__(256) void smallm_kernel(SmArgs p) {
-  constexpr int NR = SWIGLU ? 2 * R : R;  // weight rows per wave
-  constexpr int NV = R * MT;              // outputs per wave per token tile
+template <int R, int MT>
+__global__ __launch_bounds__(256) void router_kernel(RouterArgs p) {
+  constexpr int NV = R * MT;  // outputs per wave per token tile
   __shared__ float4 xs[MT][kRound / 4];
-  __shared__ int64_t tok_x[MT];
-  __shared__ int64_t tok_o[MT];
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int n0 = (blockIdx.x * 4 + wv) * R;
-
-  // which matrix and which tokens
-  int64_t e, p0, M;
-  const bool moe = p.active != nullptr;
-  if (moe) {
-    const int a = blockIdx.y;
-    if (a >= *p.n_active) return;  // uniform over the workgroup
-    e = p.active[a];
-    p0 = p.offsets[e];
-    M = p.offsets[e + 1] - p0;
-  } else {
-    e = p.expert;
-    p0 = 0;
-    M = p.M;
-  }
-  const int64_t row_bytes = int64_t(p.K) * BITS / 8;
-  const int64_t groups = BITS == 32 ? 0 : p.K / p.group;
-  const uint8_t* abase = p.a + e * p.stride;
-  const uint8_t* bbase = SWIGLU ? p.b + e * p.stride : nullptr;
-  const float2* ameta = reinterpret_cast<const float2*>(abase + p.meta_off);
-  const float2* bmeta = SWIGLU ? reinterpret_cast<const float2*>(bbase + p.meta_off) : nullptr;
   const int nrounds = (p.K + kRound - 1) / kRound;
 
-  const int64_t mstart = moe ? 0 : int64_t(blockIdx.y) * MT;
-  const int64_t mstep = moe ? MT : int64_t(gridDim.y) * MT;
-  for (int64_t m0 = mstart; m0 < M; m0 += mstep) {
-    const int mt = int(M - m0 < MT ? M - m0 : MT);
-    __syncthreads();  // previous tile fully consumed
-    if (threadIdx.x < MT) {
-      const int m = threadIdx.x;
-      int64_t xr = 0, orow = 0;
-      if (m < mt) {
-        const int64_t pidx = p0 + m0 + m;
-        if (p.xrows == XR_GATHER) xr = p.perm[pidx] / p.top_k;
-        else xr = pidx;
-        orow = pidx;
-      }
-      tok_x[m] = xr;
-      tok_o[m] = orow;
-    }
-    float acc[NR][MT];
+  for (int64_t m0 = int64_t(blockIdx.y) * MT; m0 < p.M; m0 += int64_t(gridDim.y) * MT) {
+    const int mt = int(p.M - m0 < MT ? p.M - m0 : MT);
+    float acc[R][MT];
 #pragma unroll
-    for (int j = 0; j < NR; ++j)
+    for (int j = 0; j < R; ++j)
 #pragma unroll
       for (int m = 0; m < MT; ++m) acc[j][m] = 0.0f;
 
     for (int rd = 0; rd < nrounds; ++rd) {
-      __syncthreads();
+      __syncthreads();  // previous round fully consumed
       // stage x[m][rd*1024 .. +1024) with the chunk swizzle described below
       for (int idx = threadIdx.x; idx < MT * (kRound / 4); idx += 256) {
         const int m = idx / (kRound / 4);
         const int k4 = idx % (kRound / 4);
         const int k = rd * kRound + k4 * 4;
         float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (m < mt && k < p.K) v = *reinterpret_cast<const float4*>(p.X + tok_x[m] * p.K + k);
+        if (m < mt && k < p.K) v = *reinterpret_cast<const float4*>(p.X + (m0 + m) * p.K + k);
         // lane l's 16 values are float4 slots 4l..4l+3; rotating them by
         // (l >> 2) spreads 16 lanes' reads over distinct LDS banks
         const int l = k4 >> 2, j = k4 & 3;
@@ -148,13 +66,19 @@ __global__ __launch_bounds__(256) void smallm_kernel(SmArgs p) {
       __syncthreads();
       const int chunk = rd * 64 + lane;
       if (chunk * 16 >= p.K) continue;  // this lane has no weights this round
-      float wf[NR][16];
+      float wf[R][16];
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         const int n = min(n0 + r, p.N - 1);
-        load16<BITS>(abase + n * row_bytes, ameta + n * groups, chunk, p.group, wf[r]);
-        if constexpr (SWIGLU)
-          load16<BITS>(bbase + n * row_bytes, bmeta + n * groups, chunk, p.group, wf[R + r]);
+        const float4* q = reinterpret_cast<const float4*>(p.W + int64_t(n) * p.K) + chunk * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float4 v = q[j];
+          wf[r][4 * j] = v.x;
+          wf[r][4 * j + 1] = v.y;
+          wf[r][4 * j + 2] = v.z;
+          wf[r][4 * j + 3] = v.w;
+        }
       }
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -169,7 +93,7 @@ __global__ __launch_bounds__(256) void smallm_kernel(SmArgs p) {
           xv[4 * j + 3] = v.w;
         }
 #pragma unroll
-        for (int j = 0; j < NR; ++j) {
+        for (int j = 0; j < R; ++j) {
           float d = acc[j][m];
 #pragma unroll
           for (int q = 0; q < 16; ++q) d = fmaf(xv[q], wf[j][q], d);
@@ -185,105 +109,36 @@ __global__ __launch_bounds__(256) void smallm_kernel(SmArgs p) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) va[r * MT + m] = acc[r][m];
     const float ta = wave_reduce_scatter<NV>(va);
-    float tb = 0.0f;
-    if constexpr (SWIGLU) {
-      float vb[NV];
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int m = 0; m < MT; ++m) vb[r * MT + m] = acc[R + r][m];
-      tb = wave_reduce_scatter<NV>(vb);
-    }
     if ((lane & (64 / NV - 1)) == 0) {
       const int v = reduce_scatter_row<NV>(lane);
       const int r = v / MT, m = v % MT;
       const int n = n0 + r;
       if (m < mt && n < p.N) {
         float o = ta;
-        if constexpr (SWIGLU) o = silu(ta) * tb;
         if (p.bias) o += p.bias[n];
-        p.out[tok_o[m] * p.ld_out + n] = o;
+        p.out[(m0 + m) * p.N + n] = o;
       }
     }
   }
 }
 
-static hipError_t launch_sm(const SmArgs& a, int bits, bool swiglu, int items, int64_t M,
-                            hipStream_t stream) {
-  const int MT = 8;
-  const int R = 2;
-  const int rowblocks = (a.N + 4 * R - 1) / (4 * R);
-  int gy;
-  if (a.active) {
-    gy = items;
-  } else {
-    int64_t tiles = (M + MT - 1) / MT;
-    gy = int(tiles < 65535 ? tiles : 65535);
-  }
-  if (rowblocks == 0 || gy == 0) return hipSuccess;
-  dim3 grid(rowblocks, gy);
-  if (bits == 8 && !swiglu)
-    hipLaunchKernelGGL((smallm_kernel<8, 2, 8, false>), grid, dim3(256), 0, stream, a);
-  else if (bits == 8 && swiglu)
-    hipLaunchKernelGGL((smallm_kernel<8, 2, 8, true>), grid, dim3(256), 0, stream, a);
-  else if (bits == 4 && !swiglu)
-    hipLaunchKernelGGL((smallm_kernel<4, 2, 8, false>), grid, dim3(256), 0, stream, a);
-  else if (bits == 4 && swiglu)
-    hipLaunchKernelGGL((smallm_kernel<4, 2, 8, true>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((smallm_kernel<32, 2, 8, false>), grid, dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_smallm_f32(const dsq_qweight& A, const dsq_qweight* B, int64_t expert,
-                             const Groups* grp, int xrows, const float* X, int64_t M,
-                             float* out, int64_t ld_out, hipStream_t stream) {
-  const Layout L = layout_of(A.bits, A.group, A.K, A.N);
-  SmArgs a{};
-  a.a = static_cast<const uint8_t*>(A.data);
-  a.b = B ? static_cast<const uint8_t*>(B->data) : nullptr;
-  a.stride = L.stride;
-  a.meta_off = L.meta_off;
-  a.N = int(A.N);
-  a.K = int(A.K);
-  a.group = A.group;
-  a.expert = expert;
-  a.xrows = xrows;
-  a.X = X;
-  a.M = M;
-  a.out = out;
-  a.ld_out = ld_out;
-  a.bias = nullptr;
-  int items = 1;
-  if (grp) {
-    a.active = grp->active;
-    a.n_active = grp->n_active;
-    a.offsets = grp->offsets;
-    a.perm = grp->perm;
-    a.top_k = grp->top_k;
-    items = grp->max_items;
-  }
-  return launch_sm(a, A.bits, B != nullptr, items, M, stream);
-}
-
 hipError_t launch_router(const float* X, int64_t T, const float* Wr, const float* bias,
                          int32_t E, int64_t H, float* logits, hipStream_t stream) {
-  SmArgs a{};
-  a.a = reinterpret_cast<const uint8_t*>(Wr);
-  a.b = nullptr;
-  a.stride = 0;
-  a.meta_off = 0;
+  constexpr int R = 2, MT = 8;
+  RouterArgs a{};
+  a.W = Wr;
   a.N = E;
   a.K = int(H);
-  a.group = 1;
-  a.expert = 0;
-  a.xrows = XR_DENSE;
   a.X = X;
   a.M = T;
   a.out = logits;
-  a.ld_out = E;
   a.bias = bias;
-  return launch_sm(a, 32, false, 1, T, stream);
+  const int rowblocks = (E + 4 * R - 1) / (4 * R);
+  const int64_t tiles = (T + MT - 1) / MT;
+  const int gy = int(tiles < 65535 ? tiles : 65535);
+  if (rowblocks == 0 || gy == 0) return hipSuccess;
+  hipLaunchKernelGGL((router_kernel<R, MT>), dim3(rowblocks, gy), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

@@ -152,13 +152,18 @@ dsq_status dsq_gemv(const dsq_qweight* W, int64_t expert, const float* x, float*
  *   X : fp32 [M][K] device.   Y : fp32 [M][N] device (written).
  *   math : DSQ_MATH_FP32, DSQ_MATH_BF16_MFMA or DSQ_MATH_AUTO.
  *   workspace : device scratch of dsq_gemm_workspace_bytes(M, N, K, math)
- *               bytes (may be NULL when that is 0), 256-byte aligned; its
- *               contents on entry are ignored.  It holds X in bf16 and, when
- *               the bf16 path splits K across workgroups, the fp32 partial
- *               tiles, which are added in a fixed order (deterministic).
- * FP32: |err| <= 1e-5 * sum|x w| per output.  BF16_MFMA: X and the
- * dequantized weights are rounded to bf16 and products are summed in fp32:
- * |err| <= 1e-2 * sum|x w| per output.
+ *               bytes (NULL allowed when that is 0, as for M = 1), 256-byte
+ *               aligned; its contents on entry are ignored.  BF16_MFMA: X in
+ *               bf16 and, when K is split across workgroups, the fp32 partial
+ *               tiles, added in a fixed order (deterministic).  FP32: X split
+ *               into two bf16 parts in matrix-core operand order.
+ * FP32: |err| <= 1e-5 * sum|x w| per output (M = 1 runs the GEMV; M >= 2
+ * multiplies exact integer codes by x = hi + lo, |x - hi - lo| <= 2^-18 |x|,
+ * on the matrix cores and applies zero point and scale per group in fp32).
+ * BF16_MFMA: X and the dequantized weights are rounded to bf16 and products
+ * are summed in fp32: |err| <= 1e-2 * sum|x w| per output.
+ * A workspace query of 0 for M >= 2 means the shape is beyond the limits
+ * (dsq_gemm then returns DSQ_ERR_UNSUPPORTED).
  */
 size_t dsq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t math);
 dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float* Y, int64_t M,
@@ -191,14 +196,19 @@ dsq_status dsq_moe_route_topk(const float* logits, const float* bias, int64_t T,
  *   bias     : fp32 [E] device or NULL.
  *   gate, up : packed, batch = E, N = I, K = H.  down : batch = E, N = H,
  *              K = I.  All three share bits and group.
- *   math     : as dsq_gemm, choosing by T.  The router is always fp32.
+ *   math     : as dsq_gemm, choosing by T.  The router is always fp32.  The
+ *              expert GEMMs run on the matrix cores with the weights as exact
+ *              integer codes; FP32 splits the activations (X, then h) into two
+ *              bf16 parts, BF16_MFMA rounds them to bf16.
  *   Y        : fp32 [T][H] device (written).
  *   workspace: dsq_moe_workspace_bytes(T, E, top_k, H, I, math) bytes,
  *              256-byte aligned; contents on entry are ignored.
  *   Optional outputs (NULL to skip): logits_out fp32 [T][E] (including the
  *   bias), idx_out int32 [T][k], w_out fp32 [T][k], expert_counts_out int32
  *   [E] (tokens routed to each expert; the pages log overloaded experts).
- * Limits: T <= 65536, E <= 4096, 1 <= top_k <= min(E, 32).
+ * Limits: T <= 65536, E <= 4096, 1 <= top_k <= min(E, 32); the activation
+ * tiles of the grouped GEMM must stay below 2 GiB (about T * top_k * max(H, I)
+ * * 4 bytes for FP32): dsq_moe_workspace_bytes returns 0 beyond that.
  */
 size_t dsq_moe_workspace_bytes(int64_t T, int32_t E, int32_t top_k, int64_t H, int64_t I,
                                int32_t math);
