@@ -22,6 +22,9 @@ FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-shared",
+    # every symbol must resolve at link time: a kernel whose host stub was not
+    # emitted fails the build here instead of at load time
+    "-Wl,-z,defs",
     # IEEE fp32 division and sqrt: the quantizer's codes depend on it
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-fast-math",

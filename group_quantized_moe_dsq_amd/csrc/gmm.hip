@@ -35,12 +35,14 @@
 // (one weight row: its scale and zero point are the lane's own) and rows
 // 4 (l / 16) + i, i < 4.
 //
-// Work: a wave owns NB B tiles (SwiGLU: NB/2 gate tiles and the NB/2 up
-// tiles of the same rows, so silu(g) u is formed in the lane) of one expert
-// and streams the expert's codes of those rows over all of K, D quantization
-// groups ahead; it processes up to NT token tiles per pass.  Waves take items
-// (expert, row block) in a fixed stride so every wave gets the same count to
-// within one item.
+// Work: a workgroup item is one expert and 64 (SwiGLU) or 128 output rows.
+// Each wave streams the codes of its two 16-row tiles (SwiGLU: the gate and
+// the up tile of the same rows, so silu(g) u is formed in the lane) straight
+// from HBM into its own LDS ring, 128 bytes of every row per step (whole cache
+// lines; a 16-row operand only needs 32 bytes of a row per INT4 group), and
+// the workgroup shares a ring of the token tile's activation fragments.  Three
+// steps are in flight.  Items are dealt to the workgroups in a fixed stride,
+// so every workgroup gets the same count to within one.
 #include "common.h"
 #include "internal.h"
 
@@ -62,14 +64,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(n), 0x00020000);
 }
 
-#ifndef DSQ_GMM_CODE_AUX
-#define DSQ_GMM_CODE_AUX 0
-#endif
-constexpr int kNT = 0;                    // aux: default caching
-// Codes use default caching: a 16-row tile takes 32-128 B of each row per
-// group, and the rest of the 128-byte line is used by the next groups; a
-// nontemporal hint drops it from L2 before they come.
-constexpr int kStream = DSQ_GMM_CODE_AUX;
+constexpr int kNT = 0;  // aux of the register loads: default caching
 
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   const f32x2_t v = {a, b};
@@ -218,202 +213,268 @@ struct GmmArgs {
   int rt;                   // row blocks (items) per expert
 };
 
-// Wave-uniform state of one item (expert, row block).
-struct GmmItem {
-  __amdgpu_buffer_rsrc_t rca, rma, rcb, rmb;  // codes / metadata of A and B
-  int64_t p0, M;                              // routed rows of the expert
-  int tb;                                     // its first token tile
-  int n0;                                     // first output row
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Wait until at most N of this wave's global loads are outstanding (loads
+// complete in order for this count).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier once the wave's own LDS accesses are done.  The memory
+// clobber keeps the compiler from moving LDS accesses across it; unlike
+// __syncthreads() it does not wait for the wave's outstanding global loads,
+// which are the prefetches this kernel keeps in flight.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Chunk swizzle of the code tiles in LDS: 16-byte chunk j of row r sits at
+// position j ^ swz(r), so the 16 rows an MFMA operand read touches fall on
+// distinct banks.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+template <int BITS, int J, bool SWIGLU>
+struct GmmShape {
+  static constexpr int W = 8;                       // waves per workgroup
+  static constexpr int NB = 2;                      // B tiles (16 rows) per wave
+  static constexpr int L = 1024 / (J * 32 * BITS);  // groups per 128 code bytes of a row
+  static constexpr int DM = 3;                      // ring depth in steps of L groups
+  static constexpr int CSLOT = NB * 16 * 128;       // one step of a wave's codes
+  static constexpr int MSLOT = NB * 16 * L * 8;     // one step of a wave's (scale, zp)
+  static constexpr int PPR = L >= 2 ? L / 2 : 2;    // direct-load pieces per metadata row
+  static constexpr int PB = L >= 2 ? 16 : 4;        // bytes per piece
+  static constexpr int WSLOT = CSLOT + MSLOT;
+  static constexpr int AFR = L * J * 1024;          // one step of activation fragments
+  static constexpr int ASLOT = AFR + L * 64;        // + their group sums
+  static constexpr int PER_STEP = 3 * NB + 2;       // direct loads per wave and step
+  static constexpr int LDS = W * DM * WSLOT + DM * ASLOT;
+  static constexpr int ROWS = SWIGLU ? W * 16 : W * NB * 16;  // output rows per item
+  static_assert(L * J <= 8, "one fragment load per wave and step");
+  static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-// One pass over K for the NTT token tiles starting at tile t0 of the item.
-template <int BITS, int J, int XP, int NB, int NTT, int D, bool SWIGLU>
-__device__ __forceinline__ void gmm_pass(const GmmArgs& p, const GmmItem& it,
-                                         __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rx,
-                                         const int (&voc)[NB], const int (&vom)[NB], int t0) {
-  constexpr int TPT = 16 / XP;
+// Per-item, per-lane state of the streaming loop.
+template <int NB>
+struct GmmLane {
+  __amdgpu_buffer_rsrc_t rca, rcb, rma, rmb;  // codes / (scale, zp) of A and B
+  int vdc[NB][2];  // direct-load offsets of the lane's code chunks (step 0)
+  int vdm[NB];     // direct-load offsets of the lane's metadata piece (step 0)
+  int wrow;        // first output row of the wave
+  int64_t p0, M;   // the expert's routed rows
+};
+
+// One pass of a workgroup over K for token tile `tile` (local index t):
+// wave w streams the codes and (scale, zp) of its NB tiles (SwiGLU: the gate
+// and the up tile of the same 16 rows) 128 code bytes of every row per step
+// (L groups; whole cache lines) into its own LDS ring by direct global->LDS
+// loads, and the workgroup shares a ring of the token tile's activation
+// fragments and group sums.  DM steps are in flight; one barrier per step
+// releases the oldest slot.  Nothing but these direct loads is outstanding
+// across a step, so the waits are the explicit ones below.
+template <int BITS, int J, int XP, bool SWIGLU>
+__device__ __forceinline__ void gmm_tile_pass(const GmmArgs& p, const GmmLane<2>& st,
+                                              uint8_t* wring, uint8_t* aring,
+                                              __amdgpu_buffer_rsrc_t ra,
+                                              __amdgpu_buffer_rsrc_t rx, int wv, int tile,
+                                              int t) {
+  using Sh = GmmShape<BITS, J, SWIGLU>;
+  constexpr int NB = Sh::NB, L = Sh::L, DM = Sh::DM;
+  constexpr int TPT = 16 / XP;  // tokens per tile
+  constexpr int LB = J * BITS;  // code bytes per lane, tile and group
   constexpr float kOff = BITS == 4 ? 16.0f : 0.0f;
-  constexpr int CW = J * BITS / 4;
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g4 = lane >> 4;
   const int G = p.group, S = p.K / G;
-  int voa[NTT], vox[NTT];
+  const int MS = (S + L - 1) / L;
+  const int abase = tile * S * J * 1024, xbase = tile * S * 64;
+  const bool mlane = lane < 16 * Sh::PPR;
+  f32x4_t y[NB];
 #pragma unroll
-  for (int t = 0; t < NTT; ++t) {
-    const int tile = it.tb + t0 + t;
-    voa[t] = tile * S * J * 1024 + lane * 16;
-    vox[t] = tile * S * 64 + g4 * 16;
-  }
-  f32x4_t y[NB][NTT];
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int t = 0; t < NTT; ++t) y[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < NB; ++b) y[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // ring of D groups of codes and metadata; activations one group ahead
-  uint32_t cw[D][NB][CW];
-  f32x2_t mt[D][NB];
-  auto load_codes = [&](int s, uint32_t (&w)[NB][CW], f32x2_t (&m)[NB]) {
-    const int so = s * (G * BITS / 8);
+  auto issue = [&](int m, int slot) {
+    uint8_t* ws = wring + slot * Sh::WSLOT;
+    uint8_t* as = aring + slot * Sh::ASLOT;
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const __amdgpu_buffer_rsrc_t rc = (SWIGLU && b >= NB / 2) ? it.rcb : it.rca;
-      const __amdgpu_buffer_rsrc_t rm = (SWIGLU && b >= NB / 2) ? it.rmb : it.rma;
-      if constexpr (CW == 2) {
-        const u32x2_t v = __builtin_bit_cast(
-            u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rc, voc[b], so, kStream));
-        w[b][0] = v[0];
-        w[b][1] = v[1];
-      } else {
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
-        for (int h = 0; h < CW / 4; ++h) {
-          const u32x4_t v = __builtin_bit_cast(
-              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, voc[b] + 16 * h, so, kStream));
+      for (int h = 0; h < 2; ++h)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((SWIGLU && b == 1) ? st.rcb : st.rca,
+                                                 (lds_ptr_t)(ws + b * 2048 + h * 1024), 16,
+                                                 st.vdc[b][h] + m * 128, 0, 0, 0);
+    if (mlane) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w[b][4 * h + i] = v[i];
-        }
-      }
-      m[b] = __builtin_bit_cast(f32x2_t,
-                                __builtin_amdgcn_raw_buffer_load_b64(rm, vom[b], s * 8, kNT));
+      for (int b = 0; b < NB; ++b)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((SWIGLU && b == 1) ? st.rmb : st.rma,
+                                                 (lds_ptr_t)(ws + Sh::CSLOT + b * 16 * L * 8), Sh::PB,
+                                                 st.vdm[b] + m * L * 8, 0, 0, 0);
     }
+    // one activation fragment per wave (waves beyond L*J repeat one)
+    const int f = wv % (L * J);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(as + f * 1024), 16,
+                                             abase + (m * L * J + f) * 1024 + lane * 16, 0, 0, 0);
+    if (lane < L * 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(as + Sh::AFR), 4,
+                                               xbase + m * L * 64 + lane * 4, 0, 0, 0);
   };
-  u32x4_t af[2][NTT][J];
-  f32x4_t xsum[2][NTT];
-  auto load_act = [&](int s, u32x4_t (&A)[NTT][J], f32x4_t (&X)[NTT]) {
+
+  auto compute = [&](int m, int slot) {
+    const uint8_t* ws = wring + slot * Sh::WSLOT;
+    const uint8_t* as = aring + slot * Sh::ASLOT;
 #pragma unroll
-    for (int t = 0; t < NTT; ++t) {
+    for (int sl = 0; sl < L; ++sl) {
+      if (m * L + sl >= S) break;  // last step may be partial (uniform)
+      u32x4_t af[J];
 #pragma unroll
       for (int j = 0; j < J; ++j)
-        A[t][j] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, voa[t] + j * 1024, s * J * 1024,
-                                                           kNT));
-      X[t] = __builtin_bit_cast(f32x4_t,
-                                __builtin_amdgcn_raw_buffer_load_b128(rx, vox[t], s * 64, kNT));
-    }
-  };
-#pragma unroll
-  for (int d = 0; d < D; ++d) load_codes(min(d, S - 1), cw[d], mt[d]);
-  load_act(0, af[0], xsum[0]);
-
-  for (int s0 = 0; s0 < S; s0 += 2 * D) {
-#pragma unroll
-    for (int u = 0; u < 2 * D; ++u) {
-      const int s = s0 + u;
-      if (s >= S) break;
-      const int d = u % D, cur = u & 1;
-      load_act(min(s + 1, S - 1), af[cur ^ 1], xsum[cur ^ 1]);
-      f32x4_t acc[NB][NTT];
+        af[j] = *reinterpret_cast<const u32x4_t*>(as + (sl * J + j) * 1024 + lane * 16);
+      const f32x4_t xsum = *reinterpret_cast<const f32x4_t*>(as + Sh::AFR + sl * 64 + g4 * 16);
+      const int off = sl * (G * BITS / 8) + g4 * LB;  // byte of the row
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        u32x4_t bq[J];
+        const uint8_t* row = ws + b * 2048 + c * 128;
+        uint32_t w[LB / 4];
+        if constexpr (LB == 8) {
+          const u32x2_t v =
+              *reinterpret_cast<const u32x2_t*>(row + (((off >> 4) ^ swz(c)) << 4) + (off & 15));
+          w[0] = v[0];
+          w[1] = v[1];
+        } else {
+#pragma unroll
+          for (int h = 0; h < LB / 16; ++h) {
+            const u32x4_t v =
+                *reinterpret_cast<const u32x4_t*>(row + ((((off >> 4) + h) ^ swz(c)) << 4));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[4 * h + i] = v[i];
+          }
+        }
+        const f32x2_t mq =
+            *reinterpret_cast<const f32x2_t*>(ws + Sh::CSLOT + (b * 16 + c) * L * 8 + sl * 8);
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-          if constexpr (BITS == 4) bq[j] = int4_to_bf16(cw[d][b][j]);
-          else bq[j] = int8_to_bf16(cw[d][b][2 * j], cw[d][b][2 * j + 1]);
+          u32x4_t bq;
+          if constexpr (BITS == 4) bq = int4_to_bf16(w[j]);
+          else bq = int8_to_bf16(w[2 * j], w[2 * j + 1]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[j]),
+                                                        __builtin_bit_cast(bf16x8_t, bq), acc, 0,
+                                                        0, 0);
         }
+        const float sc = mq[0], zq = mq[1] + kOff;
 #pragma unroll
-        for (int t = 0; t < NTT; ++t) {
-          acc[b][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int j = 0; j < J; ++j)
-            acc[b][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8_t, af[cur][t][j]), __builtin_bit_cast(bf16x8_t, bq[j]),
-                acc[b][t], 0, 0, 0);
-        }
+        for (int i = 0; i < 4; ++i) y[b][i] = fmaf(sc, fmaf(-zq, xsum[i], acc[i]), y[b][i]);
       }
-      // zero point and scale of the group, in fp32, after all MFMAs are issued
+    }
+  };
+
+  lds_barrier();  // every wave is done with both rings
+  issue(0, 0);
+  if (MS > 1) issue(1, 1);
+  for (int m0 = 0; m0 < MS; m0 += DM) {
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const float sc = mt[d][b][0];
-        const float zq = mt[d][b][1] + kOff;
-#pragma unroll
-        for (int t = 0; t < NTT; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            y[b][t][i] = fmaf(sc, fmaf(-zq, xsum[cur][t][i], acc[b][t][i]), y[b][t][i]);
-      }
-      load_codes(min(s + D, S - 1), cw[d], mt[d]);
+    for (int u = 0; u < DM; ++u) {
+      const int m = m0 + u;
+      if (m >= MS) break;
+      // step m has landed (step m + 1, if any, may still be in flight)
+      if (m + 1 < MS) wait_vmcnt<Sh::PER_STEP>();
+      else wait_vmcnt<0>();
+      lds_barrier();  // all waves' loads of step m landed; step m - 1 consumed
+      if (m + 2 < MS) issue(m + 2, (u + 2) % DM);
+      compute(m, u);
     }
   }
 
-  // epilogue: rows 4 g4 + i of tile t are parts of this lane's tokens
+  // epilogue: rows 4 g4 + i of the tile are parts of this lane's tokens
 #pragma unroll
-  for (int t = 0; t < NTT; ++t) {
+  for (int q = 0; q < 4 / XP; ++q) {
+    const int64_t mrow = int64_t(t) * TPT + g4 * (4 / XP) + q;
+    if (mrow >= st.M) continue;
+    const int64_t orow = p.active ? st.p0 + mrow : mrow;
+    float* o = p.out + orow * p.ld_out;
+    if constexpr (SWIGLU) {
+      const int n = st.wrow + c;
+      const float gv = XP == 2 ? y[0][2 * q] + y[0][2 * q + 1] : y[0][q];
+      const float uv = XP == 2 ? y[1][2 * q] + y[1][2 * q + 1] : y[1][q];
+      if (n < p.N) o[n] = silu(gv) * uv;
+    } else {
 #pragma unroll
-    for (int q = 0; q < 4 / XP; ++q) {
-      const int64_t m = int64_t(t0 + t) * TPT + g4 * (4 / XP) + q;
-      if (m >= it.M) continue;
-      const int64_t orow = p.active ? it.p0 + m : m;
-      float* o = p.out + orow * p.ld_out;
-#pragma unroll
-      for (int b = 0; b < (SWIGLU ? NB / 2 : NB); ++b) {
-        const int n = it.n0 + b * 16 + c;
-        if (n >= p.N) continue;
-        float v = XP == 2 ? y[b][t][2 * q] + y[b][t][2 * q + 1] : y[b][t][q];
-        if constexpr (SWIGLU) {
-          const int bu = b + NB / 2;
-          const float u = XP == 2 ? y[bu][t][2 * q] + y[bu][t][2 * q + 1] : y[bu][t][q];
-          v = silu(v) * u;
-        }
-        o[n] = v;
+      for (int b = 0; b < NB; ++b) {
+        const int n = st.wrow + 16 * b + c;
+        const float v = XP == 2 ? y[b][2 * q] + y[b][2 * q + 1] : y[b][q];
+        if (n < p.N) o[n] = v;
       }
     }
   }
 }
 
-template <int BITS, int J, int XP, int NB, int NT, int D, bool SWIGLU>
-__global__ __launch_bounds__(256) void gmm_kernel(GmmArgs p) {
-  constexpr int ROWS = SWIGLU ? NB / 2 * 16 : NB * 16;  // output rows per item
+// Workgroup items (expert, ROWS output rows) are dealt in a fixed stride.
+template <int BITS, int J, int XP, bool SWIGLU>
+__global__ __launch_bounds__(512) void gmm_kernel(GmmArgs p) {
+  using Sh = GmmShape<BITS, J, SWIGLU>;
+  constexpr int NB = Sh::NB, L = Sh::L, DM = Sh::DM;
+  constexpr int PPR = Sh::PPR, PB = Sh::PB;
+  static_assert(NB == 2, "lane state");
+  __shared__ __attribute__((aligned(16))) uint8_t sm[Sh::LDS];
   const int lane = threadIdx.x & 63;
-  const int c = lane & 15, g4 = lane >> 4;
-  const int nw = gridDim.x * 4;
-  // wave-uniform by construction; readfirstlane lets the compiler keep the
-  // item decode and the buffer descriptors in scalar registers
-  const int gw = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* const wring = sm + wv * DM * Sh::WSLOT;
+  uint8_t* const aring = sm + Sh::W * DM * Sh::WSLOT;
   const int S = p.K / p.group;
   const int64_t RB = int64_t(p.K) * BITS / 8;
   const int items = (p.active ? *p.n_active : 1) * p.rt;
   const __amdgpu_buffer_rsrc_t ra = rsrc(p.afrag, p.afrag_bytes);
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.xs, p.xs_bytes);
+  (void)c;
 
-  for (int item = gw; item < items; item += nw) {
+  for (int item = blockIdx.x; item < items; item += gridDim.x) {
     const int a = item / p.rt, rblk = item % p.rt;
-    GmmItem it;
+    GmmLane<NB> st;
     int64_t e;
+    int tb;
     if (p.active) {
       e = p.active[a];
-      it.p0 = p.offsets[e];
-      it.M = p.offsets[e + 1] - it.p0;
-      it.tb = int(it.p0 * XP / 16) + a;
+      st.p0 = p.offsets[e];
+      st.M = p.offsets[e + 1] - st.p0;
+      tb = int(st.p0 * XP / 16) + a;
     } else {
       e = p.expert;
-      it.p0 = 0;
-      it.M = p.M;
-      it.tb = 0;
+      st.p0 = 0;
+      st.M = p.M;
+      tb = 0;
     }
     const uint8_t* ea = p.wa + e * p.stride;
     const uint8_t* eb = SWIGLU ? p.wb + e * p.stride : ea;
     const int64_t cbytes = int64_t(p.N) * RB, mbytes = int64_t(p.N) * S * 8;
-    it.rca = rsrc(ea, cbytes);
-    it.rma = rsrc(ea + p.meta_off, mbytes);
-    it.rcb = rsrc(eb, cbytes);
-    it.rmb = rsrc(eb + p.meta_off, mbytes);
-    it.n0 = rblk * ROWS;
-    int voc[NB], vom[NB];
+    // tile b of the wave: matrix B (SwiGLU up) for b = 1 in SwiGLU mode, else
+    // A; rows wrow + roff(b) .. +16 with roff(b) = 0 (SwiGLU) or 16 b
+    st.rca = rsrc(ea, cbytes);
+    st.rcb = rsrc(eb, cbytes);
+    st.rma = rsrc(ea + p.meta_off, mbytes);
+    st.rmb = rsrc(eb + p.meta_off, mbytes);
+    st.wrow = rblk * Sh::ROWS + wv * (SWIGLU ? 16 : NB * 16);
+    // codes: tile b, half h -> lane reads row 8h + lane/8, global chunk
+    // (lane % 8) ^ swz(row), landing at LDS chunk lane % 8 of that row
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const int nb = it.n0 + (SWIGLU ? (b % (NB / 2)) : b) * 16 + c;
-      const int n = min(nb, p.N - 1);
-      voc[b] = int(int64_t(n) * RB) + g4 * J * BITS;
-      vom[b] = n * S * 8;
+      const int roff = SWIGLU ? 0 : 16 * b;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 8 * h + (lane >> 3);
+        const int n = min(st.wrow + roff + r, p.N - 1);
+        st.vdc[b][h] = int(int64_t(n) * RB) + (((lane & 7) ^ swz(r)) << 4);
+      }
+      // (scale, zp): LDS [tile][row][L groups] of the step; lane -> (row,
+      // piece) with 16-byte pieces for L >= 2 and words for L == 1
+      const int n = min(st.wrow + roff + lane / PPR, p.N - 1);
+      st.vdm[b] = n * S * 8 + (lane % PPR) * PB;
     }
-    const int ntiles = int((it.M * XP + 15) / 16);
-    int t0 = 0;
-    for (; t0 + NT <= ntiles; t0 += NT)
-      gmm_pass<BITS, J, XP, NB, NT, D, SWIGLU>(p, it, ra, rx, voc, vom, t0);
-    if constexpr (NT > 1) {
-      for (; t0 < ntiles; ++t0) gmm_pass<BITS, J, XP, NB, 1, D, SWIGLU>(p, it, ra, rx, voc, vom, t0);
-    }
+    const int ntiles = int((st.M * XP + 15) / 16);
+    for (int t = 0; t < ntiles; ++t)
+      gmm_tile_pass<BITS, J, XP, SWIGLU>(p, st, wring, aring, ra, rx, wv, tb + t, t);
   }
 }
 
@@ -425,15 +486,12 @@ int tiles_bound(int64_t rows, int64_t segments, int xp) {
 
 template <int BITS, int J, int XP, bool SWIGLU>
 hipError_t launch_one(const GmmArgs& a, int max_items, hipStream_t stream) {
-  constexpr int NB = 4;
-  constexpr int NT = XP == 2 ? 2 : 1;
-  constexpr int D = J * BITS <= 16 ? 4 : 2;
   const int64_t total = int64_t(max_items) * a.rt;
-  // every wave gets the same number of items to within one
-  int64_t waves = total < 2048 ? total : 2048;
-  const unsigned blocks = unsigned((waves + 3) / 4);
+  // one workgroup per CU; every workgroup gets the same number of items to
+  // within one
+  const int64_t blocks = total < 256 ? total : 256;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL((gmm_kernel<BITS, J, XP, NB, NT, D, SWIGLU>), dim3(blocks), dim3(256), 0,
+  hipLaunchKernelGGL((gmm_kernel<BITS, J, XP, SWIGLU>), dim3(unsigned(blocks)), dim3(512), 0,
                      stream, a);
   return hipGetLastError();
 }
@@ -520,7 +578,7 @@ hipError_t launch_gmm(const dsq_qweight& A, const dsq_qweight* B, int64_t expert
   a.xs_bytes = int64_t(xs_bytes);
   a.out = out;
   a.ld_out = ld_out;
-  const int rows = B ? 32 : 64;  // output rows per item (NB = 4 tiles of 16)
+  const int rows = B ? 128 : 256;  // output rows per workgroup item
   a.rt = int((A.N + rows - 1) / rows);
   if (xp == 2) return launch_bits<2>(a, A.bits, B != nullptr, items, stream);
   return launch_bits<1>(a, A.bits, B != nullptr, items, stream);
