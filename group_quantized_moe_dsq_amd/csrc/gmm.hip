@@ -65,6 +65,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t
 }
 
 constexpr int kNT = 0;  // aux of the register loads: default caching
+// Cache policy of the code loads.  Each 128-byte line of codes is consumed
+// whole by one direct load, yet the nontemporal hint measured ~15% slower
+// than default caching on this path, so the default stays.
+#ifndef DSQ_GMM_CODE_AUX
+#define DSQ_GMM_CODE_AUX 0
+#endif
+constexpr int kCodeAux = DSQ_GMM_CODE_AUX;
 
 __device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
   const f32x2_t v = {a, b};
@@ -256,61 +263,150 @@ struct GmmShape {
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-// Per-item, per-lane state of the streaming loop.
-template <int NB>
-struct GmmLane {
-  __amdgpu_buffer_rsrc_t rca, rcb, rma, rmb;  // codes / (scale, zp) of A and B
-  int vdc[NB][2];  // direct-load offsets of the lane's code chunks (step 0)
-  int vdm[NB];     // direct-load offsets of the lane's metadata piece (step 0)
-  int wrow;        // first output row of the wave
-  int64_t p0, M;   // the expert's routed rows
+// Position in a workgroup's sequence of passes: items (expert, ROWS output
+// rows) dealt in a fixed stride, each item's token tiles in order, each tile
+// one pass of MS steps over K.
+struct GmmCursor {
+  int j;           // position in the workgroup's item sequence
+  int item;        // global item index (>= items: exhausted)
+  int t, ntiles;   // token tile of the item and their count
+  int m;           // step within the pass
+  int tb;          // first token tile of the expert
+  int64_t e, p0, M;
 };
 
-// One pass of a workgroup over K for token tile `tile` (local index t):
-// wave w streams the codes and (scale, zp) of its NB tiles (SwiGLU: the gate
-// and the up tile of the same 16 rows) 128 code bytes of every row per step
-// (L groups; whole cache lines) into its own LDS ring by direct global->LDS
-// loads, and the workgroup shares a ring of the token tile's activation
-// fragments and group sums.  DM steps are in flight; one barrier per step
-// releases the oldest slot.  Nothing but these direct loads is outstanding
-// across a step, so the waits are the explicit ones below.
+// Item j of this workgroup.  Workgroup b runs on XCD b % 8; the workgroups of
+// one XCD take consecutive items (the row blocks of one or two experts) at
+// the same time, so that XCD's L2 fetches those experts' activation tiles
+// once.  Every workgroup gets the same number of items to within one.
+__device__ __forceinline__ int gmm_item(int j) {
+  const int nb = gridDim.x, b = blockIdx.x;
+  if (nb % 8 != 0) return b + j * nb;
+  const int per = nb / 8;  // workgroups per XCD
+  return (j * 8 + b % 8) * per + b / 8;
+}
+
+template <int XP>
+__device__ __forceinline__ void gmm_cursor_load(const GmmArgs& p, int items, GmmCursor& cu) {
+  cu.item = gmm_item(cu.j);
+  if (cu.item >= items) return;
+  const int a = cu.item / p.rt;
+  if (p.active) {
+    cu.e = p.active[a];
+    cu.p0 = p.offsets[cu.e];
+    cu.M = p.offsets[cu.e + 1] - cu.p0;
+    cu.tb = int(cu.p0 * XP / 16) + a;
+  } else {
+    cu.e = p.expert;
+    cu.p0 = 0;
+    cu.M = p.M;
+    cu.tb = 0;
+  }
+  cu.ntiles = int((cu.M * XP + 15) / 16);
+  cu.t = 0;
+  cu.m = 0;
+}
+
+// Advance by one step; returns true when a new item begins.
+template <int XP>
+__device__ __forceinline__ bool gmm_cursor_next(const GmmArgs& p, int items, int MS,
+                                                GmmCursor& cu) {
+  if (++cu.m < MS) return false;
+  cu.m = 0;
+  if (++cu.t < cu.ntiles) return false;
+  ++cu.j;
+  gmm_cursor_load<XP>(p, items, cu);
+  return true;
+}
+
+// The whole streaming loop of one workgroup.  Wave w streams the codes and
+// (scale, zp) of its NB tiles (SwiGLU: the gate and the up tile of the same
+// 16 rows) 128 code bytes of every row per step (L groups; whole cache lines)
+// into its own LDS ring by direct global->LDS loads, and the workgroup shares
+// a ring of the token tile's activation fragments and group sums.  The ring
+// runs on across passes and items: a lookahead cursor issues the loads two
+// steps ahead of the compute cursor, wherever those steps fall.  One barrier
+// per step releases the oldest slot; nothing but the direct loads is
+// outstanding across a step, so the waits are the explicit ones below.
 template <int BITS, int J, int XP, bool SWIGLU>
-__device__ __forceinline__ void gmm_tile_pass(const GmmArgs& p, const GmmLane<2>& st,
-                                              uint8_t* wring, uint8_t* aring,
-                                              __amdgpu_buffer_rsrc_t ra,
-                                              __amdgpu_buffer_rsrc_t rx, int wv, int tile,
-                                              int t) {
+__device__ __forceinline__ void gmm_stream(const GmmArgs& p, uint8_t* sm) {
   using Sh = GmmShape<BITS, J, SWIGLU>;
   constexpr int NB = Sh::NB, L = Sh::L, DM = Sh::DM;
   constexpr int TPT = 16 / XP;  // tokens per tile
   constexpr int LB = J * BITS;  // code bytes per lane, tile and group
   constexpr float kOff = BITS == 4 ? 16.0f : 0.0f;
+  static_assert(DM == 3, "slot arithmetic below");
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g4 = lane >> 4;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint8_t* const wring = sm + wv * DM * Sh::WSLOT;
+  uint8_t* const aring = sm + Sh::W * DM * Sh::WSLOT;
   const int G = p.group, S = p.K / G;
-  const int MS = (S + L - 1) / L;
-  const int abase = tile * S * J * 1024, xbase = tile * S * 64;
+  const int MS = (S + L - 1) / L;  // steps over K
+  const int64_t RB = int64_t(p.K) * BITS / 8;
+  const int items = (p.active ? *p.n_active : 1) * p.rt;
+  const __amdgpu_buffer_rsrc_t ra = rsrc(p.afrag, p.afrag_bytes);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(p.xs, p.xs_bytes);
   const bool mlane = lane < 16 * Sh::PPR;
-  f32x4_t y[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) y[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto wrow_of = [&](int item) {
+    return (item % p.rt) * Sh::ROWS + wv * (SWIGLU ? 16 : NB * 16);
+  };
 
-  auto issue = [&](int m, int slot) {
+  // lookahead cursor and its load state
+  GmmCursor la;
+  la.j = 0;
+  gmm_cursor_load<XP>(p, items, la);
+  if (la.item >= items) return;
+  __amdgpu_buffer_rsrc_t rca, rcb, rma, rmb;
+  int vdc[NB][2], vdm[NB];
+  auto la_item = [&]() {
+    const uint8_t* ea = p.wa + la.e * p.stride;
+    const uint8_t* eb = SWIGLU ? p.wb + la.e * p.stride : ea;
+    const int64_t cbytes = int64_t(p.N) * RB, mbytes = int64_t(p.N) * S * 8;
+    rca = rsrc(ea, cbytes);
+    rcb = rsrc(eb, cbytes);
+    rma = rsrc(ea + p.meta_off, mbytes);
+    rmb = rsrc(eb + p.meta_off, mbytes);
+    const int wrow = wrow_of(la.item);
+    // tile b of the wave: matrix B (SwiGLU up) for b = 1 in SwiGLU mode, else
+    // A; rows wrow + roff .. +16 with roff = 0 (SwiGLU) or 16 b.  Codes: half
+    // h -> lane reads row 8h + lane/8, global chunk (lane % 8) ^ swz(row),
+    // landing at LDS chunk lane % 8 of that row.  (scale, zp): lane -> (row,
+    // piece) of LDS [tile][row][L groups].
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int roff = SWIGLU ? 0 : 16 * b;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = 8 * h + (lane >> 3);
+        const int n = min(wrow + roff + r, p.N - 1);
+        vdc[b][h] = int(int64_t(n) * RB) + (((lane & 7) ^ swz(r)) << 4);
+      }
+      const int n = min(wrow + roff + lane / Sh::PPR, p.N - 1);
+      vdm[b] = n * S * 8 + (lane % Sh::PPR) * Sh::PB;
+    }
+  };
+  la_item();
+
+  auto issue = [&](int slot) {
     uint8_t* ws = wring + slot * Sh::WSLOT;
     uint8_t* as = aring + slot * Sh::ASLOT;
+    const int m = la.m;
+    const int tile = la.tb + la.t;
+    const int abase = tile * S * J * 1024, xbase = tile * S * 64;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds((SWIGLU && b == 1) ? st.rcb : st.rca,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((SWIGLU && b == 1) ? rcb : rca,
                                                  (lds_ptr_t)(ws + b * 2048 + h * 1024), 16,
-                                                 st.vdc[b][h] + m * 128, 0, 0, 0);
+                                                 vdc[b][h] + m * 128, 0, 0, kCodeAux);
     if (mlane) {
 #pragma unroll
       for (int b = 0; b < NB; ++b)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds((SWIGLU && b == 1) ? st.rmb : st.rma,
-                                                 (lds_ptr_t)(ws + Sh::CSLOT + b * 16 * L * 8), Sh::PB,
-                                                 st.vdm[b] + m * L * 8, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds((SWIGLU && b == 1) ? rmb : rma,
+                                                 (lds_ptr_t)(ws + Sh::CSLOT + b * 16 * L * 8),
+                                                 Sh::PB, vdm[b] + m * L * 8, 0, 0, 0);
     }
     // one activation fragment per wave (waves beyond L*J repeat one)
     const int f = wv % (L * J);
@@ -319,7 +415,12 @@ __device__ __forceinline__ void gmm_tile_pass(const GmmArgs& p, const GmmLane<2>
     if (lane < L * 16)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(as + Sh::AFR), 4,
                                                xbase + m * L * 64 + lane * 4, 0, 0, 0);
+    if (gmm_cursor_next<XP>(p, items, MS, la) && la.item < items) la_item();
   };
+
+  f32x4_t y[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) y[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int m, int slot) {
     const uint8_t* ws = wring + slot * Sh::WSLOT;
@@ -370,112 +471,70 @@ __device__ __forceinline__ void gmm_tile_pass(const GmmArgs& p, const GmmLane<2>
     }
   };
 
-  lds_barrier();  // every wave is done with both rings
-  issue(0, 0);
-  if (MS > 1) issue(1, 1);
-  for (int m0 = 0; m0 < MS; m0 += DM) {
+  // compute cursor
+  GmmCursor cu;
+  cu.j = 0;
+  gmm_cursor_load<XP>(p, items, cu);
+  auto epilogue = [&]() {
+    // rows 4 g4 + i of the tile are parts of this lane's tokens
+    const int wrow = wrow_of(cu.item);
+#pragma unroll
+    for (int q = 0; q < 4 / XP; ++q) {
+      const int64_t mrow = int64_t(cu.t) * TPT + g4 * (4 / XP) + q;
+      if (mrow >= cu.M) continue;
+      const int64_t orow = p.active ? cu.p0 + mrow : mrow;
+      float* o = p.out + orow * p.ld_out;
+      if constexpr (SWIGLU) {
+        const int n = wrow + c;
+        const float gv = XP == 2 ? y[0][2 * q] + y[0][2 * q + 1] : y[0][q];
+        const float uv = XP == 2 ? y[1][2 * q] + y[1][2 * q + 1] : y[1][q];
+        if (n < p.N) o[n] = silu(gv) * uv;
+      } else {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const int n = wrow + 16 * b + c;
+          const float v = XP == 2 ? y[b][2 * q] + y[b][2 * q + 1] : y[b][q];
+          if (n < p.N) o[n] = v;
+        }
+      }
+    }
+  };
+
+  // steps issued so far; step g + 1 is in flight at step g iff issued > g + 1
+  int issued = 0;
+  issue(0);
+  ++issued;
+  if (la.item < items) {
+    issue(1);
+    ++issued;
+  }
+  for (int g0 = 0;; g0 += DM) {
 #pragma unroll
     for (int u = 0; u < DM; ++u) {
-      const int m = m0 + u;
-      if (m >= MS) break;
-      // step m has landed (step m + 1, if any, may still be in flight)
-      if (m + 1 < MS) wait_vmcnt<Sh::PER_STEP>();
+      const int g = g0 + u;
+      if (g >= issued) return;  // every issued step has been computed
+      if (issued > g + 1) wait_vmcnt<Sh::PER_STEP>();
       else wait_vmcnt<0>();
-      lds_barrier();  // all waves' loads of step m landed; step m - 1 consumed
-      if (m + 2 < MS) issue(m + 2, (u + 2) % DM);
-      compute(m, u);
-    }
-  }
-
-  // epilogue: rows 4 g4 + i of the tile are parts of this lane's tokens
-#pragma unroll
-  for (int q = 0; q < 4 / XP; ++q) {
-    const int64_t mrow = int64_t(t) * TPT + g4 * (4 / XP) + q;
-    if (mrow >= st.M) continue;
-    const int64_t orow = p.active ? st.p0 + mrow : mrow;
-    float* o = p.out + orow * p.ld_out;
-    if constexpr (SWIGLU) {
-      const int n = st.wrow + c;
-      const float gv = XP == 2 ? y[0][2 * q] + y[0][2 * q + 1] : y[0][q];
-      const float uv = XP == 2 ? y[1][2 * q] + y[1][2 * q + 1] : y[1][q];
-      if (n < p.N) o[n] = silu(gv) * uv;
-    } else {
-#pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        const int n = st.wrow + 16 * b + c;
-        const float v = XP == 2 ? y[b][2 * q] + y[b][2 * q + 1] : y[b][q];
-        if (n < p.N) o[n] = v;
+      lds_barrier();  // all waves' loads of step g landed; step g - 1 consumed
+      if (la.item < items) {
+        issue((u + 2) % DM);
+        ++issued;
       }
+      compute(cu.m, u);
+      if (cu.m == MS - 1) {
+        epilogue();
+#pragma unroll
+        for (int b = 0; b < NB; ++b) y[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      gmm_cursor_next<XP>(p, items, MS, cu);
     }
   }
 }
 
-// Workgroup items (expert, ROWS output rows) are dealt in a fixed stride.
 template <int BITS, int J, int XP, bool SWIGLU>
 __global__ __launch_bounds__(512) void gmm_kernel(GmmArgs p) {
-  using Sh = GmmShape<BITS, J, SWIGLU>;
-  constexpr int NB = Sh::NB, L = Sh::L, DM = Sh::DM;
-  constexpr int PPR = Sh::PPR, PB = Sh::PB;
-  static_assert(NB == 2, "lane state");
-  __shared__ __attribute__((aligned(16))) uint8_t sm[Sh::LDS];
-  const int lane = threadIdx.x & 63;
-  const int c = lane & 15;
-  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint8_t* const wring = sm + wv * DM * Sh::WSLOT;
-  uint8_t* const aring = sm + Sh::W * DM * Sh::WSLOT;
-  const int S = p.K / p.group;
-  const int64_t RB = int64_t(p.K) * BITS / 8;
-  const int items = (p.active ? *p.n_active : 1) * p.rt;
-  const __amdgpu_buffer_rsrc_t ra = rsrc(p.afrag, p.afrag_bytes);
-  const __amdgpu_buffer_rsrc_t rx = rsrc(p.xs, p.xs_bytes);
-  (void)c;
-
-  for (int item = blockIdx.x; item < items; item += gridDim.x) {
-    const int a = item / p.rt, rblk = item % p.rt;
-    GmmLane<NB> st;
-    int64_t e;
-    int tb;
-    if (p.active) {
-      e = p.active[a];
-      st.p0 = p.offsets[e];
-      st.M = p.offsets[e + 1] - st.p0;
-      tb = int(st.p0 * XP / 16) + a;
-    } else {
-      e = p.expert;
-      st.p0 = 0;
-      st.M = p.M;
-      tb = 0;
-    }
-    const uint8_t* ea = p.wa + e * p.stride;
-    const uint8_t* eb = SWIGLU ? p.wb + e * p.stride : ea;
-    const int64_t cbytes = int64_t(p.N) * RB, mbytes = int64_t(p.N) * S * 8;
-    // tile b of the wave: matrix B (SwiGLU up) for b = 1 in SwiGLU mode, else
-    // A; rows wrow + roff(b) .. +16 with roff(b) = 0 (SwiGLU) or 16 b
-    st.rca = rsrc(ea, cbytes);
-    st.rcb = rsrc(eb, cbytes);
-    st.rma = rsrc(ea + p.meta_off, mbytes);
-    st.rmb = rsrc(eb + p.meta_off, mbytes);
-    st.wrow = rblk * Sh::ROWS + wv * (SWIGLU ? 16 : NB * 16);
-    // codes: tile b, half h -> lane reads row 8h + lane/8, global chunk
-    // (lane % 8) ^ swz(row), landing at LDS chunk lane % 8 of that row
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int roff = SWIGLU ? 0 : 16 * b;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int r = 8 * h + (lane >> 3);
-        const int n = min(st.wrow + roff + r, p.N - 1);
-        st.vdc[b][h] = int(int64_t(n) * RB) + (((lane & 7) ^ swz(r)) << 4);
-      }
-      // (scale, zp): LDS [tile][row][L groups] of the step; lane -> (row,
-      // piece) with 16-byte pieces for L >= 2 and words for L == 1
-      const int n = min(st.wrow + roff + lane / PPR, p.N - 1);
-      st.vdm[b] = n * S * 8 + (lane % PPR) * PB;
-    }
-    const int ntiles = int((st.M * XP + 15) / 16);
-    for (int t = 0; t < ntiles; ++t)
-      gmm_tile_pass<BITS, J, XP, SWIGLU>(p, st, wring, aring, ra, rx, wv, tb + t, t);
-  }
+  __shared__ __attribute__((aligned(16))) uint8_t sm[GmmShape<BITS, J, SWIGLU>::LDS];
+  gmm_stream<BITS, J, XP, SWIGLU>(p, sm);
 }
 
 namespace {
