@@ -17,7 +17,6 @@ namespace {
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 // Up to this many tokens the fp32 MoE runs each (token, slot) pair as its own
 // GEMV instead of grouping tokens by expert.
-constexpr int64_t kDecodeMaxTokens = 4;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 

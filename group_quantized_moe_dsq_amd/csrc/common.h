@@ -186,10 +186,11 @@ __device__ __forceinline__ void argmax_step(float& v, int& i) {
   const float ov = __int_as_float(__builtin_amdgcn_update_dpp(
       __float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xf, false));
   const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xf, false);
-  if (oi >= 0 && (i < 0 || ranks_before(ov, oi, v, i))) {
-    v = ov;
-    i = oi;
-  }
+  // branch-free: the comparison masks combine with bitwise ops and two selects
+  // (a branch per step costs exec-mask round trips)
+  const bool better = (oi >= 0) & ((i < 0) | (ov > v) | ((ov == v) & (oi > i)));
+  v = better ? ov : v;
+  i = better ? oi : i;
 }
 
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {

@@ -1,16 +1,28 @@
-// decode.hip -- the MoE layer for a few tokens (decode), as four launches:
-//   router GEMV (fp32) -> softmax/top-k -> gate/up GEMV + SwiGLU per routing
-//   slot -> down GEMV fused with the weighted combine.
+// decode.hip -- the MoE layer for a few tokens (decode), as three launches:
+//   router GEMV (fp32) -> gate/up + SwiGLU per routing slot (the kernel ranks
+//   the scores itself) -> down fused with the weighted combine.
 //
 // Method: "Hand-writing a DeepSeek inference engine in pure C"
-// (hnwysp.cn/news/134870) §3.5: router = linear layer + softmax + top-k, the
-// selected experts run on the token, their outputs are summed with the routing
-// weights.  With a handful of tokens every (token, slot) pair is its own
-// GEMV: grouping by expert only pays once experts are shared by many tokens.
-// The expert form down(silu(gate) * up) is the workload's definition.
+// (hnwysp.cn/news/134870) §3.2 (dequantize inside the matmul loop), §3.5
+// (router = linear layer + softmax + top-k, the selected experts run on the
+// token, their outputs are summed with the routing weights).  With a handful
+// of tokens every (token, slot) pair is its own matrix-vector product:
+// grouping by expert only pays once experts are shared by many tokens.  The
+// expert form down(silu(gate) * up) is the workload's definition.
+//
+// The expert products run on v_mfma_f32_16x16x32_bf16 like the grouped GEMM
+// (gmm.hip): the B operand holds 16 weight rows as exact bf16 integers (INT4:
+// bf16(16 + q), INT8: bf16(q)), the A operand the token's activation split
+// into two bf16 parts x = hi + lo (rows 0 and 1; rows 2..15 are zero), and
+// each group's zero point and scale are applied in fp32:
+//   sum_k x (q - zp) s = s (sum_k x (q + o) - (zp + o) sum_k x).
+// This keeps the INT4 dequantization at about one VALU operation per code
+// (the fp32 FMA form needs about three, which would make decode VALU-bound).
+// A workgroup of 8 waves owns one 16-row tile; its waves split K eight ways
+// and meet in LDS, where the parts are added in a fixed order.
 #include "common.h"
-#include "gemv_core.h"
 #include "internal.h"
+#include "mfma_util.h"
 
 namespace dsq {
 
@@ -103,28 +115,20 @@ struct DecArgs {
   float* Y;              // [T][H]
 };
 
-#ifndef DSQ_GU_RP
-#define DSQ_GU_RP 2  // gate/up output rows per wave step (2 * RP weight rows)
-#endif
-#ifndef DSQ_GU_WAVES
-#define DSQ_GU_WAVES (256 * 8)  // target waves over all slots
-#endif
-#ifndef DSQ_DN_R
-#define DSQ_DN_R 4  // down output rows per wave
-#endif
-
-constexpr int kDecodeMaxE = 1024;  // scores per lane held in registers: 16
+constexpr int kDecodeMaxE = 256;  // scores per lane held in registers: 4
+constexpr int kDecWaves = 8;       // waves per workgroup: the K split
 
 // ---------------------------------------------------------------------------
 // Top-k of one token's E scores by one wave (softmax + top-k + renormalise,
 // "Hand-writing a DeepSeek inference engine in pure C" §3.4-§3.5): k rounds
-// of a DPP wave argmax with the comparator (score desc, index desc).  Returns
-// the expert of rank `want` and its renormalised weight
-//   exp(s_want - s_max) / sum over the k selected of exp(s - s_max).
+// of a DPP wave argmax with the comparator (score desc, index desc).  Writes
+// the experts in rank order to e_out[0..k) and their renormalised weights
+//   exp(s_r - s_max) / sum over the k selected of exp(s - s_max)
+// to w_out[0..k) (LDS).
 // ---------------------------------------------------------------------------
 template <int EPL>
-__device__ __forceinline__ void topk_rank(const float* __restrict__ l, int E, int k, int want,
-                                          int lane, int* out_e, float* out_w) {
+__device__ __forceinline__ void topk_all(const float* __restrict__ l, int E, int k, int lane,
+                                         int* e_out, float* w_out) {
   float v[EPL];
   uint32_t taken = 0;
   // all loads first (clamped addresses, no branches), then the fix-ups
@@ -136,257 +140,491 @@ __device__ __forceinline__ void topk_rank(const float* __restrict__ l, int E, in
     if (v[j] != v[j]) v[j] = -INFINITY;  // NaN ranks last
     if (e >= E) taken |= 1u << j;
   }
-  float best = 0.0f, mine = 0.0f, sum = 0.0f;
-  int mine_e = 0;
+  float best = 0.0f, mine = 0.0f;
   for (int r = 0; r < k; ++r) {
     float bv = -INFINITY;
     int bi = -1;
 #pragma unroll
     for (int j = 0; j < EPL; ++j) {
       const int e = lane + 64 * j;
-      if (!((taken >> j) & 1u) && (bi < 0 || ranks_before(v[j], e, bv, bi))) {
-        bv = v[j];
-        bi = e;
-      }
+      const bool better = !((taken >> j) & 1u) & ((bi < 0) | (v[j] > bv) | ((v[j] == bv) & (e > bi)));
+      bv = better ? v[j] : bv;
+      bi = better ? e : bi;
     }
     wave_argmax(bv, bi);  // uniform across the wave
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (r == 0) best = bv;
-    const float ex = expf(bv - best);
-    sum += ex;
-    if (r == want) {
-      mine = ex;
-      mine_e = bi;
-    }
+    if (lane == r) mine = bv;
+    if (lane == 0) e_out[r] = bi;
   }
-  *out_e = mine_e;
-  *out_w = mine / sum;
+  const float ex = lane < k ? expf(mine - best) : 0.0f;
+  const float sum = wave_sum(ex);
+  if (lane < k) w_out[lane] = ex / sum;
 }
 
 // ---------------------------------------------------------------------------
-// gate/up + SwiGLU: one routing slot j = t*k + i per blockIdx.y.  Wave 0
-// first ranks token t's scores to find the slot's expert (the workgroups
-// with blockIdx.x == 0 also publish idx/w for the down kernel).  Then each
-// wave walks blocks of RP output rows n, computing gate row n and up row n
-// of that expert against X[t] (staged in LDS, sliced into registers), and
-// writes h[j][n] = silu(g) * u.  The next row block's loads are issued
-// before the current one's math.
+// Activation parts in LDS: rows of x (fp32) -> xp[row][part][K] bf16 (part 0:
+// hi = bf16(x), part 1: lo = bf16(x - hi)) and xs[row][group] = (sum of hi,
+// sum of lo, 0, 0) over the group, the sums taken in double and rounded once.
+// The A operand of lane (c, g4) is row c < 2 of this layout; the group-sum
+// operand of lane g4 = 0 is the float4 itself, all other lanes read zeros.
 // ---------------------------------------------------------------------------
-template <int BITS, int RP, int KCH>
-__global__ __launch_bounds__(256) void gateup_gemv_kernel(DecArgs p) {
-  constexpr int NR = 2 * RP;
-  extern __shared__ float4 xl[];
-  __shared__ int s_e;
-  const int lane = threadIdx.x & 63;
-  const int slot = blockIdx.y;
-  const int t = slot / p.k;
-  if (threadIdx.x < 64) {
-    int e;
-    float wgt;
-    topk_rank<kDecodeMaxE / 64>(p.logits + int64_t(t) * p.E, p.E, p.k, slot % p.k, lane, &e,
-                                &wgt);
-    if (lane == 0) {
-      s_e = e;
-      if (blockIdx.x == 0) {
-        p.idx[slot] = e;
-        p.w[slot] = wgt;
+__device__ __forceinline__ void stage_parts(const float* __restrict__ src, int64_t ld,
+                                            const int32_t* __restrict__ rows, int nrows, int K,
+                                            int G, uint16_t* xp, float4* xs, int tid,
+                                            int nthreads) {
+  constexpr int U = 4;     // segments per thread in flight
+  const int segs = K / 8;  // multiple of G / 8: a group's lanes are adjacent
+  const int total = nrows * segs;
+  for (int base = tid; base < total; base += U * nthreads) {
+    float4 qa[U], qb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {  // all loads first (clamped), then the work
+      const int it = min(base + u * nthreads, total - 1);
+      const int r = it / segs, sg = it % segs;
+      const int64_t row = rows ? rows[r] : r;
+      const float4* q = reinterpret_cast<const float4*>(src + row * ld + sg * 8);
+      qa[u] = q[0];
+      qb[u] = q[1];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int it = base + u * nthreads;
+      if (it >= total) break;  // whole groups leave together: total is a multiple of G / 8
+      const int r = it / segs, sg = it % segs;
+      const float v[8] = {qa[u].x, qa[u].y, qa[u].z, qa[u].w, qb[u].x, qb[u].y, qb[u].z, qb[u].w};
+      uint32_t hw[4], lw[4];
+      double sh = 0.0, sl = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 h0 = __bf16(v[2 * i]), h1 = __bf16(v[2 * i + 1]);
+        const __bf16 l0 = __bf16(v[2 * i] - float(h0)), l1 = __bf16(v[2 * i + 1] - float(h1));
+        hw[i] = uint32_t(__builtin_bit_cast(uint16_t, h0)) |
+                (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
+        lw[i] = uint32_t(__builtin_bit_cast(uint16_t, l0)) |
+                (uint32_t(__builtin_bit_cast(uint16_t, l1)) << 16);
+        sh += double(float(h0)) + double(float(h1));
+        sl += double(float(l0)) + double(float(l1));
       }
+      for (int o = 1; o < G / 8; o <<= 1) {
+        sh += __shfl_xor(sh, o);
+        sl += __shfl_xor(sl, o);
+      }
+      uint4* d = reinterpret_cast<uint4*>(xp + (int64_t(r) * 2) * K + sg * 8);
+      d[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      d[K / 8] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      if ((sg * 8) % G == 0)
+        xs[r * (K / G) + sg * 8 / G] = make_float4(float(sh), float(sl), 0.f, 0.f);
     }
-  }
-  __syncthreads();
-  const int e = s_e;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nwaves = gridDim.x * 4;
-  const int row_bytes = p.H * BITS / 8;
-  const int nchunk = row_bytes / 16;
-  const int groups = p.H / p.group;
-  const uint8_t* gbase = p.gate + int64_t(e) * p.gu_stride;
-  const uint8_t* ubase = p.up + int64_t(e) * p.gu_stride;
-  const float2* gmeta = reinterpret_cast<const float2*>(gbase + p.gu_meta_off);
-  const float2* umeta = reinterpret_cast<const float2*>(ubase + p.gu_meta_off);
-
-  auto load = [&](RowChunks<BITS, NR, KCH>& C, int n0) {
-    const uint8_t* prow[NR];
-    const float2* mrow[NR];
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      const int n = min(n0 + r, p.I - 1);
-      prow[r] = gbase + int64_t(n) * row_bytes;
-      mrow[r] = gmeta + int64_t(n) * groups;
-      prow[RP + r] = ubase + int64_t(n) * row_bytes;
-      mrow[RP + r] = umeta + int64_t(n) * groups;
-    }
-    C.load(prow, mrow, nchunk, p.group, lane);
-  };
-  XSlice<BITS, KCH> xs;
-  auto finish = [&](const RowChunks<BITS, NR, KCH>& C, int n0) {
-    float acc[NR];
-    C.dot(xs, acc);
-    float g[RP], u[RP];
-#pragma unroll
-    for (int r = 0; r < RP; ++r) {
-      g[r] = acc[r];
-      u[r] = acc[RP + r];
-    }
-    const float tg = wave_reduce_scatter<RP>(g);
-    const float tu = wave_reduce_scatter<RP>(u);
-    if ((lane & (64 / RP - 1)) == 0) {
-      const int n = n0 + reduce_scatter_row<RP>(lane);
-      if (n < p.I) p.hbuf[int64_t(slot) * p.I + n] = silu(tg) * tu;
-    }
-  };
-
-  RowChunks<BITS, NR, KCH> A, B;
-  const int step = nwaves * RP;
-  int n0 = wave * RP;
-  if (n0 < p.I) load(A, n0);
-  stage_lds<Codes<BITS>::kPerChunk / 4>(p.X + int64_t(t) * p.H, p.H, xl);
-  __syncthreads();
-  xs.load_lds(xl, nchunk, lane);
-  xs.sums();
-  while (n0 < p.I) {
-    const int n1 = n0 + step;
-    if (n1 < p.I) load(B, n1);
-    finish(A, n0);
-    if (n1 >= p.I) break;
-    const int n2 = n1 + step;
-    if (n2 < p.I) load(A, n2);
-    finish(B, n1);
-    n0 = n2;
   }
 }
 
 // ---------------------------------------------------------------------------
-// down + combine: one token per blockIdx.y; the token's k vectors h[t*k+i]
-// are staged in LDS once per workgroup.  Each wave owns R output rows and,
-// for each of the token's k slots in order, adds
-//   w[t][i] * (h[t*k+i] . Wd_{idx[t][i]}[n])
-// to its per-lane partial sums before one reduction per row.  The next
-// slot's weights are loaded while the current slot is computed.  No atomics:
-// the result is deterministic.
+// Streaming a wave's share of NT weight tiles (16 rows each) through its own
+// LDS ring.  The wave's share is groups [s_lo, s_hi) of every row; a step is
+// the next 128 code bytes of every row (L groups), fetched by direct
+// global->LDS loads: 16-byte chunk j of row r lands at position j ^ swz(r) of
+// the row, so the MFMA operand reads (16 rows at once) fall on distinct
+// banks; the rows' (scale, zp) of the step land beside them.  DEPTH steps are
+// in flight; only this wave reads its ring, so no barrier is needed.
 // ---------------------------------------------------------------------------
-template <int BITS, int R, int KCH>
-__global__ __launch_bounds__(256) void down_combine_kernel(DecArgs p) {
-  constexpr int F = Codes<BITS>::kPerChunk / 4;
-  extern __shared__ float4 hl[];
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.y;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int n0 = wave * R;
-  const int row_bytes = p.I * BITS / 8;
-  const int nchunk = row_bytes / 16;
-  const int groups = p.I / p.group;
-  const bool active = n0 < p.H;
+__device__ __forceinline__ int dswz(int r) { return (r >> 1) & 7; }
 
-  auto load = [&](RowChunks<BITS, R, KCH>& C, int i) {
-    const int e = p.idx[t * p.k + i];
-    const uint8_t* dbase = p.down + int64_t(e) * p.d_stride;
-    const float2* dmeta = reinterpret_cast<const float2*>(dbase + p.d_meta_off);
-    const uint8_t* prow[R];
-    const float2* mrow[R];
+template <int BITS, int J, int NT>
+struct DecRing {
+  static constexpr int L = 1024 / (J * 32 * BITS);  // groups per step
+  static constexpr int LB = J * BITS;                 // code bytes per lane, tile and group
+  static constexpr int CSLOT = NT * 2048;
+  static constexpr int WSLOT = CSLOT + NT * 16 * L * 8;
+  static constexpr int DEPTH = 3;  // a deeper down ring measured no faster
+  static constexpr int PPR = L >= 2 ? L / 2 : 2;      // direct-load pieces per metadata row
+  static constexpr int PB = L >= 2 ? 16 : 4;          // bytes per piece
+  static constexpr int PER_STEP = 3 * NT;             // direct loads per step
+  static constexpr int BYTES = DEPTH * WSLOT;         // LDS per wave
+};
+
+// Per-lane offsets of a wave's tiles (step 0 of its share).
+template <int BITS, int J, int NT>
+struct DecLane {
+  __amdgpu_buffer_rsrc_t rc[NT], rm[NT];
+  int vdc[NT][2];
+  int vdm[NT];
+};
+
+template <int BITS, int J, int NT>
+__device__ __forceinline__ void dec_lane(DecLane<BITS, J, NT>& ln, const uint8_t* const (&mat)[NT],
+                                         int64_t meta_off, int N, int K, int G, int row0,
+                                         int s_lo, int lane) {
+  using R = DecRing<BITS, J, NT>;
+  const int S = K / G;
+  const int64_t RB = int64_t(K) * BITS / 8;
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int n = min(n0 + r, p.H - 1);
-      prow[r] = dbase + int64_t(n) * row_bytes;
-      mrow[r] = dmeta + int64_t(n) * groups;
+  for (int b = 0; b < NT; ++b) {
+    ln.rc[b] = rsrc(mat[b], int64_t(N) * RB);
+    ln.rm[b] = rsrc(mat[b] + meta_off, int64_t(N) * S * 8);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = 8 * h + (lane >> 3);
+      const int n = min(row0 + r, N - 1);
+      ln.vdc[b][h] = int(int64_t(n) * RB) + s_lo * (G * BITS / 8) + (((lane & 7) ^ dswz(r)) << 4);
     }
-    C.load(prow, mrow, nchunk, p.group, lane);
-  };
-  RowChunks<BITS, R, KCH> A, B;
-  if (active) load(A, 0);
-  for (int i = 0; i < p.k; ++i)
-    stage_lds<F>(p.hbuf + int64_t(t * p.k + i) * p.I, p.I, hl + int64_t(i) * (p.I / 4));
-  __syncthreads();
-  if (!active) return;  // after the only barrier
-
-  float acc[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
-  auto accumulate = [&](const RowChunks<BITS, R, KCH>& C, int i) {
-    XSlice<BITS, KCH> xs;
-    xs.load_lds(hl + int64_t(i) * (p.I / 4), nchunk, lane);
-    xs.sums();
-    float part[R];
-    C.dot(xs, part);
-    const float wgt = p.w[t * p.k + i];
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = fmaf(wgt, part[r], acc[r]);
-  };
-  for (int i = 0; i < p.k; i += 2) {
-    if (i + 1 < p.k) load(B, i + 1);
-    accumulate(A, i);
-    if (i + 1 >= p.k) break;
-    if (i + 2 < p.k) load(A, i + 2);
-    accumulate(B, i + 1);
+    const int n = min(row0 + lane / R::PPR, N - 1);
+    ln.vdm[b] = (n * S + s_lo) * 8 + (lane % R::PPR) * R::PB;
   }
-  const float s = wave_reduce_scatter<R>(acc);
-  if ((lane & (64 / R - 1)) == 0) {
-    const int n = n0 + reduce_scatter_row<R>(lane);
-    if (n < p.H) p.Y[int64_t(t) * p.H + n] = s;
+}
+
+template <int BITS, int J, int NT>
+__device__ __forceinline__ void dec_issue(const DecLane<BITS, J, NT>& ln, uint8_t* slot, int m,
+                                          int lane) {
+  using R = DecRing<BITS, J, NT>;
+#pragma unroll
+  for (int b = 0; b < NT; ++b)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ln.rc[b], (lds_ptr_t)(slot + b * 2048 + h * 1024),
+                                               16, ln.vdc[b][h] + m * 128, 0, 0, 0);
+  if (lane < 16 * R::PPR) {
+#pragma unroll
+    for (int b = 0; b < NT; ++b)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ln.rm[b],
+                                               (lds_ptr_t)(slot + R::CSLOT + b * 16 * R::L * 8),
+                                               R::PB, ln.vdm[b] + m * R::L * 8, 0, 0, 0);
+  }
+}
+
+// Products of step m of the wave's share: for every group s of the step
+// (below s_hi), y[b] += the group's fp32 correction of the MFMA sum of the
+// activation parts (rows 0, 1 of A) times tile b's codes.
+template <int BITS, int J, int NT>
+__device__ __forceinline__ void dec_step(const uint8_t* slot, f32x4_t (&y)[NT], const uint16_t* xp,
+                                         const float4* xs, int K, int G, int s_lo, int s_hi,
+                                         int m, int lane, const uint32_t* zeros) {
+  using R = DecRing<BITS, J, NT>;
+  constexpr float kOff = BITS == 4 ? 16.0f : 0.0f;
+  const int c = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int sl = 0; sl < R::L; ++sl) {
+    const int s = s_lo + m * R::L + sl;
+    if (s >= s_hi) break;  // uniform
+    u32x4_t af[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int k = s * G + g4 * 8 * J + 8 * j;
+      const uint16_t* a = c < 2 ? xp + int64_t(c) * K + k : reinterpret_cast<const uint16_t*>(zeros);
+      af[j] = *reinterpret_cast<const u32x4_t*>(a);
+    }
+    const float4 x4 = g4 == 0 ? xs[s] : *reinterpret_cast<const float4*>(zeros);
+    const int off = sl * (G * BITS / 8) + g4 * R::LB;  // byte of the 128-byte window
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+      const uint8_t* row = slot + b * 2048 + c * 128;
+      uint32_t w[R::LB / 4];
+      if constexpr (R::LB == 8) {
+        const u32x2_t v =
+            *reinterpret_cast<const u32x2_t*>(row + (((off >> 4) ^ dswz(c)) << 4) + (off & 15));
+        w[0] = v[0];
+        w[1] = v[1];
+      } else {
+#pragma unroll
+        for (int h = 0; h < R::LB / 16; ++h) {
+          const u32x4_t v =
+              *reinterpret_cast<const u32x4_t*>(row + ((((off >> 4) + h) ^ dswz(c)) << 4));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[4 * h + i] = v[i];
+        }
+      }
+      const f32x2_t mq =
+          *reinterpret_cast<const f32x2_t*>(slot + R::CSLOT + (b * 16 + c) * R::L * 8 + sl * 8);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        u32x4_t bq;
+        if constexpr (BITS == 4) bq = int4_to_bf16(w[j]);
+        else bq = int8_to_bf16(w[2 * j], w[2 * j + 1]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[j]),
+                                                      __builtin_bit_cast(bf16x8_t, bq), acc, 0, 0,
+                                                      0);
+      }
+      const float sc = mq[0], zq = mq[1] + kOff;
+      y[b][0] = fmaf(sc, fmaf(-zq, x4.x, acc[0]), y[b][0]);
+      y[b][1] = fmaf(sc, fmaf(-zq, x4.y, acc[1]), y[b][1]);
+    }
+  }
+}
+
+// A wave's ring of streamed steps.  Steps are numbered over the wave's whole
+// sequence (units one after another), so the loads of the next unit are in
+// flight while the current unit is reduced.
+template <int BITS, int J, int NT>
+struct DecStream {
+  using R = DecRing<BITS, J, NT>;
+  uint8_t* ring;
+  int issued = 0;     // steps issued
+  int consumed = 0;   // steps computed
+  __device__ __forceinline__ uint8_t* slot(int g) const { return ring + (g % R::DEPTH) * R::WSLOT; }
+  // Wait for the oldest outstanding step (the one about to be computed).
+  __device__ __forceinline__ void wait_oldest() const {
+    const int ahead = issued - consumed - 1;  // steps issued after it
+    if (ahead >= 4) wait_vmcnt<4 * R::PER_STEP>();
+    else if (ahead == 3) wait_vmcnt<3 * R::PER_STEP>();
+    else if (ahead == 2) wait_vmcnt<2 * R::PER_STEP>();
+    else if (ahead == 1) wait_vmcnt<R::PER_STEP>();
+    else wait_vmcnt<0>();
+  }
+};
+
+// ---------------------------------------------------------------------------
+// gate/up + SwiGLU.  Every workgroup first ranks the scores of the T tokens
+// (wave t ranks token t; workgroup 0 publishes idx/w for the down kernel).
+// Units (slot j = t*k + i, 16-row tile) are dealt to the workgroups in a
+// fixed stride (token-major, so a workgroup restages the activation parts
+// only when the token changes); within a unit, wave w streams groups
+// [w*GP, (w+1)*GP) of K of the gate and the up tile, and the eight partial
+// sums of each row meet in LDS.
+// ---------------------------------------------------------------------------
+template <int BITS, int J>
+__global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
+  using R = DecRing<BITS, J, 2>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+  __shared__ int s_e[4 * 32];
+  __shared__ float s_w[4 * 32];
+  __shared__ float red[kDecWaves][2][16];
+  __shared__ __attribute__((aligned(16))) uint32_t zeros[4];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g4 = lane >> 4;
+  const int H = p.H, I = p.I, G = p.group, S = H / G, k = p.k;
+  uint8_t* rings = dsm;                                                      // [8][DEPTH][WSLOT]
+  uint16_t* xp = reinterpret_cast<uint16_t*>(dsm + kDecWaves * R::BYTES);    // [2][H]
+  float4* xs = reinterpret_cast<float4*>(dsm + kDecWaves * R::BYTES + 4 * H);  // [S]
+
+  if (threadIdx.x < 4) zeros[threadIdx.x] = 0u;
+  // waves 0..T-1 rank the tokens' scores while the others stage token 0
+  if (wv < T)
+    topk_all<kDecodeMaxE / 64>(p.logits + int64_t(wv) * p.E, p.E, k, lane, s_e + wv * k,
+                               s_w + wv * k);
+  else
+    stage_parts(p.X, H, nullptr, 1, H, G, xp, xs, threadIdx.x - 64 * T, 512 - 64 * T);
+  __syncthreads();
+  if (blockIdx.x == 0 && threadIdx.x < T * k) {
+    p.idx[threadIdx.x] = s_e[threadIdx.x];
+    p.w[threadIdx.x] = s_w[threadIdx.x];
+  }
+
+  const int tiles = (I + 15) / 16;
+  const int units = T * k * tiles;
+  const int GP = (S + kDecWaves - 1) / kDecWaves;  // groups per wave
+  const int s_lo = min(S, wv * GP), s_hi = min(S, s_lo + GP);
+  const int NS = (GP + R::L - 1) / R::L;           // steps per unit
+  auto unit_of = [&](int j) { return int(blockIdx.x) + j * int(gridDim.x); };
+  if (unit_of(0) >= units) return;
+
+  DecStream<BITS, J, 2> st;
+  st.ring = rings + wv * R::BYTES;
+  // lookahead position (unit index j, step m) and its lane offsets
+  int lj = 0, lm = 0;
+  DecLane<BITS, J, 2> ln;
+  auto lane_for = [&](int j) {
+    const int u = unit_of(j);
+    const int e = s_e[u / tiles];
+    const uint8_t* const mat[2] = {p.gate + int64_t(e) * p.gu_stride,
+                                   p.up + int64_t(e) * p.gu_stride};
+    dec_lane<BITS, J, 2>(ln, mat, p.gu_meta_off, I, H, G, (u % tiles) * 16, s_lo, lane);
+  };
+  lane_for(0);
+  auto issue_next = [&]() {
+    if (unit_of(lj) >= units) return;
+    dec_issue<BITS, J, 2>(ln, st.slot(st.issued), lm, lane);
+    ++st.issued;
+    if (++lm == NS) {
+      lm = 0;
+      ++lj;
+      if (unit_of(lj) < units) lane_for(lj);
+    }
+  };
+  for (int d = 0; d < R::DEPTH - 1; ++d) issue_next();
+
+  int staged = 0;
+  for (int j = 0; unit_of(j) < units; ++j) {
+    const int u = unit_of(j);
+    const int slot_j = u / tiles, t = slot_j / k;
+    if (t != staged) {
+      lds_barrier();  // the previous token's parts are no longer read
+      stage_parts(p.X + int64_t(t) * H, H, nullptr, 1, H, G, xp, xs, threadIdx.x, 512);
+      lds_barrier();
+      staged = t;
+    }
+    f32x4_t y[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    for (int m = 0; m < NS; ++m) {
+      issue_next();  // into the slot computed in the previous iteration
+      st.wait_oldest();
+      dec_step<BITS, J, 2>(st.slot(st.consumed), y, xp, xs, H, G, s_lo, s_hi, m, lane, zeros);
+      ++st.consumed;
+    }
+    // rows 0 and 1 of the tile are the two parts of the token's product
+    if (g4 == 0) {
+      red[wv][0][c] = y[0][0] + y[0][1];
+      red[wv][1][c] = y[1][0] + y[1][1];
+    }
+    lds_barrier();
+    if (wv == 0 && lane < 16) {
+      float gs = 0.0f, us = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) {
+        gs += red[w][0][lane];
+        us += red[w][1][lane];
+      }
+      const int n = (u % tiles) * 16 + lane;
+      if (n < I) p.hbuf[int64_t(slot_j) * I + n] = silu(gs) * us;
+    }
+    lds_barrier();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// down + combine: Y[t][n] = sum_i w[t][i] (h[t*k+i] . Wd_{idx[t][i]}[n]).
+// Units (token t, 16-row tile of H) are dealt in a fixed stride; a workgroup
+// stages the token's k activation parts, wave w streams groups [w*GP,
+// (w+1)*GP) of I of each slot's tile in slot order, weights each slot's
+// partial sum by w[t][i], and the eight waves' sums meet in LDS in a fixed
+// order.
+// ---------------------------------------------------------------------------
+template <int BITS, int J>
+__global__ __launch_bounds__(512) void dec_down_kernel(DecArgs p, int T) {
+  using R = DecRing<BITS, J, 1>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+  __shared__ float red[kDecWaves][16];
+  __shared__ __attribute__((aligned(16))) uint32_t zeros[4];
+  __shared__ int32_t s_rows[32];
+  __shared__ int32_t s_e[4 * 32];  // routing of the T tokens, read once
+  __shared__ float s_w[4 * 32];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, g4 = lane >> 4;
+  const int H = p.H, I = p.I, G = p.group, S = I / G, k = p.k;
+  uint8_t* rings = dsm;                                                       // [8][DEPTH][WSLOT]
+  uint16_t* hp = reinterpret_cast<uint16_t*>(dsm + kDecWaves * R::BYTES);     // [k][2][I]
+  float4* hs = reinterpret_cast<float4*>(dsm + kDecWaves * R::BYTES + int64_t(k) * 4 * I);
+  if (threadIdx.x < 4) zeros[threadIdx.x] = 0u;
+  if (threadIdx.x < T * k) {
+    s_e[threadIdx.x] = p.idx[threadIdx.x];
+    s_w[threadIdx.x] = p.w[threadIdx.x];
+  }
+  __syncthreads();
+
+  const int tiles = (H + 15) / 16;
+  const int units = T * tiles;
+  const int GP = (S + kDecWaves - 1) / kDecWaves;
+  const int s_lo = min(S, wv * GP), s_hi = min(S, s_lo + GP);
+  const int NS = (GP + R::L - 1) / R::L;  // steps per slot
+  auto unit_of = [&](int j) { return int(blockIdx.x) + j * int(gridDim.x); };
+  if (unit_of(0) >= units) return;
+
+  DecStream<BITS, J, 1> st;
+  st.ring = rings + wv * R::BYTES;
+  // lookahead position (unit j, slot i, step m)
+  int lj = 0, li = 0, lm = 0;
+  DecLane<BITS, J, 1> ln;
+  auto lane_for = [&](int j, int i) {
+    const int u = unit_of(j);
+    const int t = u / tiles;
+    const int e = s_e[t * k + i];
+    const uint8_t* const mat[1] = {p.down + int64_t(e) * p.d_stride};
+    dec_lane<BITS, J, 1>(ln, mat, p.d_meta_off, H, I, G, (u % tiles) * 16, s_lo, lane);
+  };
+  lane_for(0, 0);
+  auto issue_next = [&]() {
+    if (unit_of(lj) >= units) return;
+    dec_issue<BITS, J, 1>(ln, st.slot(st.issued), lm, lane);
+    ++st.issued;
+    if (++lm == NS) {
+      lm = 0;
+      if (++li == k) {
+        li = 0;
+        ++lj;
+      }
+      if (unit_of(lj) < units) lane_for(lj, li);
+    }
+  };
+  for (int d = 0; d < R::DEPTH - 1; ++d) issue_next();
+
+  int staged = -1;
+  for (int j = 0; unit_of(j) < units; ++j) {
+    const int u = unit_of(j);
+    const int t = u / tiles;
+    if (t != staged) {
+      lds_barrier();  // the previous token's parts are no longer read
+      if (threadIdx.x < k) s_rows[threadIdx.x] = t * k + threadIdx.x;
+      lds_barrier();
+      stage_parts(p.hbuf, I, s_rows, k, I, G, hp, hs, threadIdx.x, 512);
+      lds_barrier();
+      staged = t;
+    }
+    float yacc = 0.0f;
+    for (int i = 0; i < k; ++i) {
+      f32x4_t y[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
+      for (int m = 0; m < NS; ++m) {
+        issue_next();  // into the slot computed in the previous iteration
+        st.wait_oldest();
+        dec_step<BITS, J, 1>(st.slot(st.consumed), y, hp + int64_t(i) * 2 * I,
+                             hs + int64_t(i) * S, I, G, s_lo, s_hi, m, lane, zeros);
+        ++st.consumed;
+      }
+      yacc = fmaf(s_w[t * k + i], y[0][0] + y[0][1], yacc);
+    }
+    if (g4 == 0) red[wv][c] = yacc;
+    lds_barrier();
+    if (wv == 0 && lane < 16) {
+      float v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kDecWaves; ++w) v += red[w][lane];
+      const int nn = (u % tiles) * 16 + lane;
+      if (nn < H) p.Y[int64_t(t) * H + nn] = v;
+    }
+    lds_barrier();
   }
 }
 
 namespace {
 
-template <int BITS, int KCH>
+template <int BITS, int J>
 hipError_t go_decode(const DecArgs& a, int64_t T, hipStream_t stream) {
-  constexpr int RP = DSQ_GU_RP;
-  const int64_t slots = T * a.k;
-  const int rowblocks = (a.I + RP - 1) / RP;
-  // Waves per slot, rounded down to whole workgroups so the grid never
-  // exceeds one round of resident waves (a second round would start only when
-  // the first finishes and doubles the kernel time).
-  int64_t wps = DSQ_GU_WAVES / slots;
-  if (wps > rowblocks) wps = rowblocks;
-  int bx = int(wps / 4);
-  if (bx < 1) bx = 1;
-  hipLaunchKernelGGL((gateup_gemv_kernel<BITS, RP, KCH>), dim3(bx, unsigned(slots)), dim3(256),
-                     size_t(a.H) * 4, stream, a);
+  const int64_t gu_units = T * a.k * ((a.I + 15) / 16);
+  const unsigned gb = unsigned(gu_units < 256 ? gu_units : 256);
+  const size_t gu_lds = size_t(kDecWaves) * DecRing<BITS, J, 2>::BYTES + size_t(4) * a.H +
+                        size_t(a.H / a.group) * 16;
+  // more than 64 KiB of dynamic LDS must be granted to the kernel explicitly
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dec_gateup_kernel<BITS, J>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(gu_lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dec_gateup_kernel<BITS, J>), dim3(gb), dim3(512), gu_lds, stream, a,
+                     int(T));
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t dn_units = T * ((a.H + 15) / 16);
+  const unsigned db = unsigned(dn_units < 256 ? dn_units : 256);
+  const size_t dn_lds = size_t(kDecWaves) * DecRing<BITS, J, 1>::BYTES + size_t(a.k) * 4 * a.I +
+                        size_t(a.k) * (a.I / a.group) * 16;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dec_down_kernel<BITS, J>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, int(dn_lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dec_down_kernel<BITS, J>), dim3(db), dim3(512), dn_lds, stream, a, int(T));
   return hipGetLastError();
-}
-
-template <int BITS, int KCH>
-hipError_t go_down(const DecArgs& a, int64_t T, hipStream_t stream) {
-  constexpr int R = DSQ_DN_R;
-  const int waves = (a.H + R - 1) / R;
-  const int bx = (waves + 3) / 4;
-  hipLaunchKernelGGL((down_combine_kernel<BITS, R, KCH>), dim3(bx, unsigned(T)), dim3(256),
-                     size_t(a.k) * a.I * 4, stream, a);
-  return hipGetLastError();
-}
-
-template <int BITS>
-hipError_t dispatch_gateup(const DecArgs& a, int64_t T, hipStream_t s) {
-  const int kch = (a.H * BITS / 8 / 16 + 63) / 64;
-  switch (kch) {
-    case 1: return go_decode<BITS, 1>(a, T, s);
-    case 2: return go_decode<BITS, 2>(a, T, s);
-    case 3: return go_decode<BITS, 3>(a, T, s);
-    case 4: return go_decode<BITS, 4>(a, T, s);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <int BITS>
-hipError_t dispatch_down(const DecArgs& a, int64_t T, hipStream_t s) {
-  const int kch = (a.I * BITS / 8 / 16 + 63) / 64;
-  switch (kch) {
-    case 1: return go_down<BITS, 1>(a, T, s);
-    case 2: return go_down<BITS, 2>(a, T, s);
-    default: return hipErrorInvalidValue;
-  }
 }
 
 }  // namespace
 
-// True when the decode kernels apply: a row's x slice fits the register
-// budget (at most 4 chunk rounds per lane for K = H and for K = I), the
-// scores of a token fit one wave's registers, and the token's k vectors h fit
-// the 64 KiB of LDS the down kernel stages them in.
+// True when the decode kernels apply: the wave rings plus one token's
+// activation parts (gate/up) or its k activation parts (down) fit LDS, the
+// scores of a token fit one wave's registers and k fits the rank tables.
 bool decode_supported(int bits, int64_t H, int64_t I, int32_t E, int32_t k) {
-  const int64_t a = (H * bits / 8 / 16 + 63) / 64;
-  const int64_t b = (I * bits / 8 / 16 + 63) / 64;
-  return a <= 4 && b <= 2 && E <= kDecodeMaxE && int64_t(k) * I * 4 <= 65536 && H * 4 <= 65536;
+  if (bits != 4 && bits != 8) return false;
+  // largest rings over the supported groupings (at most 4 groups per step)
+  const int64_t gu_ring = int64_t(kDecWaves) * 3 * (2 * 2048 + 2 * 16 * 4 * 8);
+  const int64_t dn_ring = int64_t(kDecWaves) * 3 * (2048 + 16 * 4 * 8);
+  const int64_t gu = gu_ring + 4 * H + (H / 64) * 16;
+  const int64_t dn = dn_ring + int64_t(k) * (4 * I + (I / 64) * 16);
+  const int64_t budget = 156 * 1024;  // 160 KiB less the static tables
+  return E <= kDecodeMaxE && k <= 32 && gu <= budget && dn <= budget;
 }
 
 hipError_t launch_moe_decode(const dsq_qweight& gate, const dsq_qweight& up,
@@ -414,9 +652,9 @@ hipError_t launch_moe_decode(const dsq_qweight& gate, const dsq_qweight& up,
   a.w = w;
   a.hbuf = hbuf;
   a.Y = Y;
-  hipError_t e = gate.bits == 8 ? dispatch_gateup<8>(a, T, stream) : dispatch_gateup<4>(a, T, stream);
-  if (e != hipSuccess) return e;
-  return gate.bits == 8 ? dispatch_down<8>(a, T, stream) : dispatch_down<4>(a, T, stream);
+  const bool g64 = gate.group == 64;
+  if (gate.bits == 8) return g64 ? go_decode<8, 2>(a, T, stream) : go_decode<8, 4>(a, T, stream);
+  return g64 ? go_decode<4, 2>(a, T, stream) : go_decode<4, 4>(a, T, stream);
 }
 
 }  // namespace dsq

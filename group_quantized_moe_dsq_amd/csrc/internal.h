@@ -47,10 +47,11 @@ hipError_t launch_combine(const float* ybuf, const int32_t* pos, const float* w,
                           int32_t k, int64_t H, float* Y, hipStream_t stream);
 
 // Decode path (few tokens): fp32 router GEMV, and the expert FFN per routing
-// slot (gate/up GEMV + SwiGLU into hbuf [T*k][I], then down GEMV fused with
-// the weighted combine into Y).
+// slot on the matrix cores (gate/up + SwiGLU into hbuf [T*k][I], then down
+// fused with the weighted combine into Y).
 hipError_t launch_router_gemv(const float* X, int64_t T, const float* Wr, const float* bias,
                               int32_t E, int64_t H, float* logits, hipStream_t stream);
+constexpr int64_t kDecodeMaxTokens = 4;  // decode kernels: at most this many tokens
 bool decode_supported(int bits, int64_t H, int64_t I, int32_t E, int32_t k);
 // Ranks each token's scores itself (writing idx/w), so no separate top-k.
 hipError_t launch_moe_decode(const dsq_qweight& gate, const dsq_qweight& up,
