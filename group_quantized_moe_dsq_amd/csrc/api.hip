@@ -201,7 +201,7 @@ size_t dsq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t math) {
   if (M < 0 || N <= 0 || K <= 0) return 0;
   if (math != DSQ_MATH_FP32 && math != DSQ_MATH_BF16_MFMA && math != DSQ_MATH_AUTO) return 0;
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim || !mul_ok(M, K) || !mul_ok(M, N)) return 0;
-  if (use_bf16(math, M)) return gemm_mfma_workspace(M, N, K);
+  if (use_bf16(math, M)) return gemm_mfma_supported(M, N, K) ? gemm_mfma_workspace(M, N, K) : 0;
   if (M < 2) return 0;  // GEMV
   // fp32 path: the token tiles of the grouped GEMM (one segment), sized for
   // the smallest supported group
@@ -222,7 +222,7 @@ dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float*
   if (M > kMaxDim || !mul_ok(M, W->K) || !mul_ok(M, W->N)) return DSQ_ERR_OVERFLOW;
   if (!aligned(X, 16) || !aligned(Y, 4)) return DSQ_ERR_ALIGN;
   const bool bf16 = use_bf16(math, M);
-  if (M >= 2) {
+  if (M >= 2 || bf16) {
     const size_t need = dsq_gemm_workspace_bytes(M, W->N, W->K, math);
     if (need == 0) return DSQ_ERR_UNSUPPORTED;
     if (!workspace || workspace_bytes < need) return DSQ_ERR_WORKSPACE;

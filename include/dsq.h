@@ -152,18 +152,21 @@ dsq_status dsq_gemv(const dsq_qweight* W, int64_t expert, const float* x, float*
  *   X : fp32 [M][K] device.   Y : fp32 [M][N] device (written).
  *   math : DSQ_MATH_FP32, DSQ_MATH_BF16_MFMA or DSQ_MATH_AUTO.
  *   workspace : device scratch of dsq_gemm_workspace_bytes(M, N, K, math)
- *               bytes (NULL allowed when that is 0, as for M = 1), 256-byte
- *               aligned; its contents on entry are ignored.  BF16_MFMA: X in
- *               bf16 and, when K is split across workgroups, the fp32 partial
- *               tiles, added in a fixed order (deterministic).  FP32: X split
- *               into two bf16 parts in matrix-core operand order.
+ *               bytes (NULL allowed when that is 0, as for FP32 with M = 1),
+ *               256-byte aligned; its contents on entry are ignored.
+ *               BF16_MFMA: X rounded to bf16 and, when K is split across
+ *               workgroups, the fp32 partial tiles, added in a fixed order
+ *               (deterministic).
+ *               FP32: X split into two bf16 parts in matrix-core operand
+ *               order.
  * FP32: |err| <= 1e-5 * sum|x w| per output (M = 1 runs the GEMV; M >= 2
  * multiplies exact integer codes by x = hi + lo, |x - hi - lo| <= 2^-18 |x|,
  * on the matrix cores and applies zero point and scale per group in fp32).
  * BF16_MFMA: X and the dequantized weights are rounded to bf16 and products
  * are summed in fp32: |err| <= 1e-2 * sum|x w| per output.
- * A workspace query of 0 for M >= 2 means the shape is beyond the limits
- * (dsq_gemm then returns DSQ_ERR_UNSUPPORTED).
+ * A workspace query of 0 for M >= 2 (or for BF16_MFMA) means the shape is
+ * beyond the limits (dsq_gemm then returns DSQ_ERR_UNSUPPORTED); BF16_MFMA
+ * needs M*K*2 and N*K below 2^31.
  */
 size_t dsq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t math);
 dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float* Y, int64_t M,
