@@ -5,21 +5,20 @@
 // inference engine in pure C", hnwysp.cn/news/134870, §3.2-§3.3) for prompt
 // tokens processed together.
 //
-// Two kernels (three with split-K):
-//   * x_to_bf16: X is rounded to bf16 once, so the GEMM reads 2 bytes per
-//     element and each X line fetched from L2 serves 64 elements;
+// Two kernels (one when K is not split):
 //   * gemm_mfma_kernel: one workgroup per 128x128 output tile and K slice,
 //     12 waves in two roles.  Waves 0-3 only read LDS and issue MFMAs (wave
 //     (wm, wn) owns 64x64 as 2x2 v_mfma_f32_32x32x16_bf16 tiles); waves 4-11
-//     load the next K steps (64 k each) from global memory into registers,
-//     dequantize the codes to bf16 and write the X and W tiles to LDS.  Two
-//     producer waves share each SIMD with one MFMA wave, so the dequant VALU
-//     work overlaps the matrix core;
+//     load the next K steps (64 k each) of X (fp32) and of the codes into
+//     registers, round X to bf16, dequantize the codes to bf16 and write both
+//     tiles to LDS.  Two producer waves share each SIMD with one MFMA wave,
+//     so the dequant VALU work overlaps the matrix core;
 //   * splitk_reduce_kernel: adds the K slices' partial tiles in slice order.
 //
-// The L2 sees a request per cache line touched by a wave's load, and the
-// loop is bound by that request rate, so every access is shaped to need few:
-//   * X: each load instruction reads 8 whole 128-byte row pieces;
+// The loop is bound by LDS (it accepts ~76 B/clk of writes and ~118 B/clk of
+// reads per CU) and by the L2, which sees a request per cache line touched
+// by a wave's load; every access is shaped to need few:
+//   * X: each load instruction reads 4 whole 256-byte row pieces;
 //   * W: a row's 64 codes of a step are one 64-byte (INT8) or 32-byte (INT4)
 //     piece, read by 4 adjacent lanes;
 //   * (scale, zp): the K slice's groups of the tile's 128 rows are copied to
@@ -56,7 +55,7 @@ constexpr int kConsumers = 4;       // MFMA waves
 constexpr int kProducers = 8;       // load / dequantize waves
 constexpr int kThreads = 64 * (kConsumers + kProducers);
 #ifndef DSQ_GEMM_STAGES
-#define DSQ_GEMM_STAGES 2
+#define DSQ_GEMM_STAGES 3
 #endif
 constexpr int kStages = DSQ_GEMM_STAGES;  // global-load steps in flight
 constexpr int kBufs = 3;                  // LDS step buffers
@@ -73,7 +72,7 @@ constexpr int kMaxWorkgroups = DSQ_GEMM_MAX_WG;  // one per CU
 struct GemmArgs {
   const uint8_t* w;     // packed entry (codes)
   const float2* meta;   // its (scale, zp) table
-  const uint16_t* Xb;   // [M][K] bf16
+  const float* X;       // [M][K] fp32
   float* Y;             // [M][N]
   float* partial;       // [tiles][SK][128*128] fp32 (split-K only)
   int M, N, K, lg;      // lg = log2(group)
@@ -85,13 +84,13 @@ struct GemmArgs {
 __device__ __forceinline__ int chunk_off(int r, int c) { return r * kRowBytes + ((c ^ (r & 7)) << 4); }
 
 // Per producer thread (t = threadIdx.x - 256, 0..511) share of one K step:
-//   X : rows (t / 8) + 64 j (j = 0, 1), 16-byte chunk t % 8 (8 bf16);
+//   X : rows (t / 16) + 32 j (j = 0..3), 4 fp32 at k = 4 (t % 16);
 //   W : row t / 4, 16 codes at k = 16 (t % 4) (INT8: one 16-byte load, INT4:
 //       one 8-byte load of two words) and the (scale, zp) of their group (a
 //       step lies inside one group), read from LDS.
 template <int BITS>
 struct StepRegs {
-  u32x4_t x[2];
+  f32x4_t x[4];
   uint32_t c[BITS == 8 ? 4 : 2];
   f32x2_t m;
 };
@@ -104,7 +103,7 @@ struct StepRegs {
 constexpr uint32_t kOOB = 0x80000000u;
 struct ProdLane {
   __amdgpu_buffer_rsrc_t rx, rw;
-  uint32_t vx[2];  // X byte offsets of (row (t / 8) + 64 j, chunk t % 8) at k = 0
+  uint32_t vx[4];  // X byte offsets of (row (t / 16) + 32 j, k = 4 (t % 16)) at k = 0
   uint32_t vw;     // code byte offset of (row t / 4, k = 16 (t % 4)) at k = 0
   const float2* ml;  // LDS (scale, zp) of row t / 4, group g_first
   int g_first;
@@ -114,9 +113,9 @@ template <int BITS>
 __device__ __forceinline__ void load_step(const ProdLane& pl, int k0, int lg, bool live,
                                           StepRegs<BITS>& r) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 4; ++j)
     r.x[j] = __builtin_bit_cast(
-        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(pl.rx, live ? pl.vx[j] : kOOB, k0 * 2, kNT));
+        f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(pl.rx, live ? pl.vx[j] : kOOB, k0 * 4, kNT));
   const uint32_t vw = live ? pl.vw : kOOB;
   if constexpr (BITS == 8) {
     const u32x4_t v = __builtin_bit_cast(
@@ -136,14 +135,15 @@ __device__ __forceinline__ void load_step(const ProdLane& pl, int k0, int lg, bo
   r.m[1] = m.y;
 }
 
-// Dequantize the step's codes and write the X and W tiles to LDS.
+// Round X to bf16, dequantize the codes and write both tiles of the step to LDS.
 template <int BITS>
 __device__ __forceinline__ void store_step(const StepRegs<BITS>& r, uint8_t* lds_a,
                                            uint8_t* lds_b) {
   const int t = threadIdx.x - 64 * kConsumers;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    *reinterpret_cast<u32x4_t*>(lds_a + chunk_off((t >> 3) + 64 * j, t & 7)) = r.x[j];
+  for (int j = 0; j < 4; ++j)
+    *reinterpret_cast<uint2*>(lds_a + chunk_off((t >> 4) + 32 * j, (t & 15) >> 1) + 8 * (t & 1)) =
+        make_uint2(pk_bf16(r.x[j][0], r.x[j][1]), pk_bf16(r.x[j][2], r.x[j][3]));
   // w = q * s - zp * s, rounded once to bf16
   const float sc = r.m[0], nzs = -r.m[1] * r.m[0];
   float f[16];
@@ -224,12 +224,12 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs p) {
   if (producer) {
     const int t = threadIdx.x - 64 * kConsumers;
     ProdLane pl;
-    pl.rx = rsrc(p.Xb, int64_t(p.M) * p.K * 2);
+    pl.rx = rsrc(p.X, int64_t(p.M) * p.K * 4);
     pl.rw = rsrc(p.w, int64_t(p.N) * p.K * BITS / 8);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int m = tm * kBM + (t >> 3) + 64 * j;
-      pl.vx[j] = m < p.M ? uint32_t((m * p.K + 8 * (t & 7)) * 2) : kOOB;
+    for (int j = 0; j < 4; ++j) {
+      const int m = tm * kBM + (t >> 4) + 32 * j;
+      pl.vx[j] = m < p.M ? uint32_t((m * p.K + 4 * (t & 15)) * 4) : kOOB;
     }
     const int row = t >> 2;
     const int n = min(tn * kBN + row, p.N - 1);
@@ -414,17 +414,6 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   *reinterpret_cast<fv*>(Y + i) = v;
 }
 
-// Xb = bf16(X), 8 elements per thread (K % 8 == 0).
-__global__ __launch_bounds__(256) void x_to_bf16_kernel(const float* __restrict__ X,
-                                                        uint16_t* __restrict__ Xb, int64_t n8) {
-  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < n8; i += int64_t(gridDim.x) * 256) {
-    const float4 a = reinterpret_cast<const float4*>(X)[2 * i];
-    const float4 b = reinterpret_cast<const float4*>(X)[2 * i + 1];
-    reinterpret_cast<uint4*>(Xb)[i] =
-        make_uint4(pk_bf16(a.x, a.y), pk_bf16(a.z, a.w), pk_bf16(b.x, b.y), pk_bf16(b.z, b.w));
-  }
-}
-
 namespace {
 
 struct Plan {
@@ -450,13 +439,11 @@ Plan plan(int64_t M, int64_t N, int64_t K, int group) {
   return pl;
 }
 
-int64_t xb_bytes(int64_t M, int64_t K) { return align256(M * K * 2); }
-
 }  // namespace
 
 bool gemm_mfma_supported(int64_t M, int64_t N, int64_t K) {
-  // 32-bit buffer offsets into bf16 X and into an INT8 entry's codes
-  return M * K * 2 < (int64_t(1) << 31) && N * K < (int64_t(1) << 31) && K % kBK == 0;
+  // 32-bit buffer offsets into X and into an INT8 entry's codes
+  return M * K * 4 < (int64_t(1) << 31) && N * K < (int64_t(1) << 31) && K % kBK == 0;
 }
 
 size_t gemm_mfma_workspace(int64_t M, int64_t N, int64_t K) {
@@ -465,8 +452,9 @@ size_t gemm_mfma_workspace(int64_t M, int64_t N, int64_t K) {
   const Plan p2 = plan(M, N, K, 128);
   const int64_t tiles = int64_t(pl.tiles_m) * pl.tiles_n;
   const int sk = max(pl.SK, p2.SK);
-  int64_t b = xb_bytes(M, K);
-  if (sk > 1) b += align256(tiles * sk * kBM * kBN * 4);
+  // at least one aligned block, so that 0 can mean "unsupported"
+  int64_t b = 256;
+  if (sk > 1) b = align256(tiles * sk * kBM * kBN * 4);
   return size_t(b);
 }
 
@@ -475,19 +463,11 @@ hipError_t launch_gemm_mfma(const dsq_qweight& W, int64_t expert, const float* X
   const Plan pl = plan(M, W.N, W.K, W.group);
   const QMat q = entry(W, expert);
   const int64_t tiles = int64_t(pl.tiles_m) * pl.tiles_n;
-  uint16_t* Xb = static_cast<uint16_t*>(workspace);
-  float* partial =
-      pl.SK > 1 ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + xb_bytes(M, W.K))
-                : nullptr;
-  const int64_t n8 = M * W.K / 8;
-  const int64_t xblocks = (n8 + 255) / 256 < 4096 ? (n8 + 255) / 256 : 4096;
-  hipLaunchKernelGGL(x_to_bf16_kernel, dim3(unsigned(xblocks)), dim3(256), 0, stream, X, Xb, n8);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  float* partial = pl.SK > 1 ? static_cast<float*>(workspace) : nullptr;
   GemmArgs a{};
   a.w = q.payload;
   a.meta = q.meta;
-  a.Xb = Xb;
+  a.X = X;
   a.Y = Y;
   a.partial = partial;
   a.M = int(M);
@@ -502,7 +482,7 @@ hipError_t launch_gemm_mfma(const dsq_qweight& W, int64_t expert, const float* X
     hipLaunchKernelGGL(gemm_mfma_kernel<8>, dim3(blocks), dim3(kThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(gemm_mfma_kernel<4>, dim3(blocks), dim3(kThreads), 0, stream, a);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess || pl.SK == 1) return e;
   const int64_t outs = M * W.N;
   if (W.N % 4 == 0)

@@ -59,9 +59,9 @@ hipError_t launch_moe_decode(const dsq_qweight& gate, const dsq_qweight& up,
                              int32_t k, const float* logits, int32_t* idx, float* w, float* hbuf,
                              float* Y, hipStream_t stream);
 
-// bf16 MFMA dense GEMM (prefill): the workspace holds X in bf16 and, when
-// the K range is split, the fp32 partial tiles.  Supported while bf16 X and
-// one weight entry stay below 2 GiB (32-bit buffer offsets).
+// bf16 MFMA dense GEMM (prefill): the workspace holds the fp32 partial
+// tiles when the K range is split.  Supported while X and one weight entry
+// stay below 2 GiB (32-bit buffer offsets).
 bool gemm_mfma_supported(int64_t M, int64_t N, int64_t K);
 size_t gemm_mfma_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_mfma(const dsq_qweight& W, int64_t expert, const float* X, float* Y,

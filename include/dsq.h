@@ -154,9 +154,8 @@ dsq_status dsq_gemv(const dsq_qweight* W, int64_t expert, const float* x, float*
  *   workspace : device scratch of dsq_gemm_workspace_bytes(M, N, K, math)
  *               bytes (NULL allowed when that is 0, as for FP32 with M = 1),
  *               256-byte aligned; its contents on entry are ignored.
- *               BF16_MFMA: X rounded to bf16 and, when K is split across
- *               workgroups, the fp32 partial tiles, added in a fixed order
- *               (deterministic).
+ *               BF16_MFMA: when K is split across workgroups, the fp32
+ *               partial tiles, added in a fixed order (deterministic).
  *               FP32: X split into two bf16 parts in matrix-core operand
  *               order.
  * FP32: |err| <= 1e-5 * sum|x w| per output (M = 1 runs the GEMV; M >= 2
@@ -166,7 +165,7 @@ dsq_status dsq_gemv(const dsq_qweight* W, int64_t expert, const float* x, float*
  * are summed in fp32: |err| <= 1e-2 * sum|x w| per output.
  * A workspace query of 0 for M >= 2 (or for BF16_MFMA) means the shape is
  * beyond the limits (dsq_gemm then returns DSQ_ERR_UNSUPPORTED); BF16_MFMA
- * needs M*K*2 and N*K below 2^31.
+ * needs M*K*4 and N*K below 2^31.
  */
 size_t dsq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t math);
 dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float* Y, int64_t M,
