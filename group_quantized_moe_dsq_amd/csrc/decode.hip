@@ -115,8 +115,18 @@ struct DecArgs {
   float* Y;              // [T][H]
 };
 
+#ifndef DSQ_DEC_GU_DEPTH
+#define DSQ_DEC_GU_DEPTH 2
+#endif
+#ifndef DSQ_DEC_DN_DEPTH
+#define DSQ_DEC_DN_DEPTH 2
+#endif
+#ifndef DSQ_DEC_UB
+#define DSQ_DEC_UB 4
+#endif
 constexpr int kDecodeMaxE = 256;  // scores per lane held in registers: 4
 constexpr int kDecWaves = 8;       // waves per workgroup: the K split
+constexpr int kDecUB = DSQ_DEC_UB; // gate/up units whose sums are added together
 
 // ---------------------------------------------------------------------------
 // Top-k of one token's E scores by one wave (softmax + top-k + renormalise,
@@ -169,64 +179,93 @@ __device__ __forceinline__ void topk_all(const float* __restrict__ l, int E, int
 // The A operand of lane (c, g4) is row c < 2 of this layout; the group-sum
 // operand of lane g4 = 0 is the float4 itself, all other lanes read zeros.
 // ---------------------------------------------------------------------------
+// One pass of the staging: up to U segments (8 values) per thread, loads
+// first (clamped addresses), converted and stored by stage_store.  A kernel
+// can issue the loads early and store after other work.
+constexpr int kStageU = 4;
+struct StageRegs {
+  float4 qa[kStageU], qb[kStageU];
+};
+
+__device__ __forceinline__ void stage_load(const float* __restrict__ src, int64_t ld,
+                                           const int32_t* __restrict__ rows, int nrows, int K,
+                                           int base, int nthreads, StageRegs& q) {
+  const int segs = K / 8;
+  const int total = nrows * segs;
+#pragma unroll
+  for (int u = 0; u < kStageU; ++u) {
+    const int it = min(base + u * nthreads, total - 1);
+    const int r = it / segs, sg = it % segs;
+    const int64_t row = rows ? rows[r] : r;
+    const float4* v = reinterpret_cast<const float4*>(src + row * ld + sg * 8);
+    q.qa[u] = v[0];
+    q.qb[u] = v[1];
+  }
+}
+
+__device__ __forceinline__ void stage_store(const StageRegs& q, int nrows, int K, int G,
+                                            uint16_t* xp, float4* xs, int base, int nthreads) {
+  const int segs = K / 8;  // multiple of G / 8: a group's lanes are adjacent
+  const int total = nrows * segs;
+#pragma unroll
+  for (int u = 0; u < kStageU; ++u) {
+    const int it = base + u * nthreads;
+    if (it >= total) break;  // whole groups leave together: total is a multiple of G / 8
+    const int r = it / segs, sg = it % segs;
+    const float v[8] = {q.qa[u].x, q.qa[u].y, q.qa[u].z, q.qa[u].w,
+                        q.qb[u].x, q.qb[u].y, q.qb[u].z, q.qb[u].w};
+    uint32_t hw[4], lw[4];
+    double sh = 0.0, sl = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const __bf16 h0 = __bf16(v[2 * i]), h1 = __bf16(v[2 * i + 1]);
+      const __bf16 l0 = __bf16(v[2 * i] - float(h0)), l1 = __bf16(v[2 * i + 1] - float(h1));
+      hw[i] = uint32_t(__builtin_bit_cast(uint16_t, h0)) |
+              (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
+      lw[i] = uint32_t(__builtin_bit_cast(uint16_t, l0)) |
+              (uint32_t(__builtin_bit_cast(uint16_t, l1)) << 16);
+      sh += double(float(h0)) + double(float(h1));
+      sl += double(float(l0)) + double(float(l1));
+    }
+    for (int o = 1; o < G / 8; o <<= 1) {
+      sh += __shfl_xor(sh, o);
+      sl += __shfl_xor(sl, o);
+    }
+    uint4* d = reinterpret_cast<uint4*>(xp + (int64_t(r) * 2) * K + sg * 8);
+    d[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    d[K / 8] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    if ((sg * 8) % G == 0)
+      xs[r * (K / G) + sg * 8 / G] = make_float4(float(sh), float(sl), 0.f, 0.f);
+  }
+}
+
+// true when one pass (kStageU segments per thread) stages nrows rows of K
+__host__ __device__ constexpr bool stage_one_pass(int64_t nrows, int64_t K, int nthreads) {
+  return nrows * (K / 8) <= int64_t(kStageU) * nthreads;
+}
+
 __device__ __forceinline__ void stage_parts(const float* __restrict__ src, int64_t ld,
                                             const int32_t* __restrict__ rows, int nrows, int K,
                                             int G, uint16_t* xp, float4* xs, int tid,
                                             int nthreads) {
-  constexpr int U = 4;     // segments per thread in flight
-  const int segs = K / 8;  // multiple of G / 8: a group's lanes are adjacent
-  const int total = nrows * segs;
-  for (int base = tid; base < total; base += U * nthreads) {
-    float4 qa[U], qb[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {  // all loads first (clamped), then the work
-      const int it = min(base + u * nthreads, total - 1);
-      const int r = it / segs, sg = it % segs;
-      const int64_t row = rows ? rows[r] : r;
-      const float4* q = reinterpret_cast<const float4*>(src + row * ld + sg * 8);
-      qa[u] = q[0];
-      qb[u] = q[1];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int it = base + u * nthreads;
-      if (it >= total) break;  // whole groups leave together: total is a multiple of G / 8
-      const int r = it / segs, sg = it % segs;
-      const float v[8] = {qa[u].x, qa[u].y, qa[u].z, qa[u].w, qb[u].x, qb[u].y, qb[u].z, qb[u].w};
-      uint32_t hw[4], lw[4];
-      double sh = 0.0, sl = 0.0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const __bf16 h0 = __bf16(v[2 * i]), h1 = __bf16(v[2 * i + 1]);
-        const __bf16 l0 = __bf16(v[2 * i] - float(h0)), l1 = __bf16(v[2 * i + 1] - float(h1));
-        hw[i] = uint32_t(__builtin_bit_cast(uint16_t, h0)) |
-                (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
-        lw[i] = uint32_t(__builtin_bit_cast(uint16_t, l0)) |
-                (uint32_t(__builtin_bit_cast(uint16_t, l1)) << 16);
-        sh += double(float(h0)) + double(float(h1));
-        sl += double(float(l0)) + double(float(l1));
-      }
-      for (int o = 1; o < G / 8; o <<= 1) {
-        sh += __shfl_xor(sh, o);
-        sl += __shfl_xor(sl, o);
-      }
-      uint4* d = reinterpret_cast<uint4*>(xp + (int64_t(r) * 2) * K + sg * 8);
-      d[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      d[K / 8] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      if ((sg * 8) % G == 0)
-        xs[r * (K / G) + sg * 8 / G] = make_float4(float(sh), float(sl), 0.f, 0.f);
-    }
+  const int total = nrows * (K / 8);
+  for (int base = tid; base < total; base += kStageU * nthreads) {
+    StageRegs q;
+    stage_load(src, ld, rows, nrows, K, base, nthreads, q);
+    stage_store(q, nrows, K, G, xp, xs, base, nthreads);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Streaming a wave's share of NT weight tiles (16 rows each) through its own
-// LDS ring.  The wave's share is groups [s_lo, s_hi) of every row; a step is
-// the next 128 code bytes of every row (L groups), fetched by direct
-// global->LDS loads: 16-byte chunk j of row r lands at position j ^ swz(r) of
-// the row, so the MFMA operand reads (16 rows at once) fall on distinct
-// banks; the rows' (scale, zp) of the step land beside them.  DEPTH steps are
-// in flight; only this wave reads its ring, so no barrier is needed.
+// LDS ring.  A step is 128 code bytes (L groups) of every row; step m of wave
+// w is piece 8 m + w of the rows, so at each step the workgroup's eight waves
+// read one contiguous kilobyte of every row together (a DRAM row is opened
+// once, not once per wave).  The pieces are fetched by direct global->LDS
+// loads: 16-byte chunk j of row r lands at position j ^ swz(r) of the row, so
+// the MFMA operand reads (16 rows at once) fall on distinct banks; the rows'
+// (scale, zp) of the step land beside them.  DEPTH steps are in flight; only
+// this wave reads its ring, so no barrier is needed.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int dswz(int r) { return (r >> 1) & 7; }
 
@@ -236,7 +275,7 @@ struct DecRing {
   static constexpr int LB = J * BITS;                 // code bytes per lane, tile and group
   static constexpr int CSLOT = NT * 2048;
   static constexpr int WSLOT = CSLOT + NT * 16 * L * 8;
-  static constexpr int DEPTH = 3;  // a deeper down ring measured no faster
+  static constexpr int DEPTH = NT == 2 ? DSQ_DEC_GU_DEPTH : DSQ_DEC_DN_DEPTH;  // steps per ring
   static constexpr int PPR = L >= 2 ? L / 2 : 2;      // direct-load pieces per metadata row
   static constexpr int PB = L >= 2 ? 16 : 4;          // bytes per piece
   static constexpr int PER_STEP = 3 * NT;             // direct loads per step
@@ -282,19 +321,21 @@ __device__ __forceinline__ void dec_issue(const DecLane<BITS, J, NT>& ln, uint8_
 #pragma unroll
     for (int h = 0; h < 2; ++h)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ln.rc[b], (lds_ptr_t)(slot + b * 2048 + h * 1024),
-                                               16, ln.vdc[b][h] + m * 128, 0, 0, 0);
+                                               16, ln.vdc[b][h] + m * (kDecWaves * 128), 0, 0, 0);
   if (lane < 16 * R::PPR) {
 #pragma unroll
     for (int b = 0; b < NT; ++b)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ln.rm[b],
                                                (lds_ptr_t)(slot + R::CSLOT + b * 16 * R::L * 8),
-                                               R::PB, ln.vdm[b] + m * R::L * 8, 0, 0, 0);
+                                               R::PB, ln.vdm[b] + m * (kDecWaves * R::L * 8), 0, 0,
+                                               0);
   }
 }
 
-// Products of step m of the wave's share: for every group s of the step
-// (below s_hi), y[b] += the group's fp32 correction of the MFMA sum of the
-// activation parts (rows 0, 1 of A) times tile b's codes.
+// Products of step m of the wave's share (groups s_lo + 8 L m .. + L, s_lo =
+// L w): for every group s of the step below s_hi, y[b] += the group's fp32
+// correction of the MFMA sum of the activation parts (rows 0, 1 of A) times
+// tile b's codes.
 template <int BITS, int J, int NT>
 __device__ __forceinline__ void dec_step(const uint8_t* slot, f32x4_t (&y)[NT], const uint16_t* xp,
                                          const float4* xs, int K, int G, int s_lo, int s_hi,
@@ -304,7 +345,7 @@ __device__ __forceinline__ void dec_step(const uint8_t* slot, f32x4_t (&y)[NT], 
   const int c = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int sl = 0; sl < R::L; ++sl) {
-    const int s = s_lo + m * R::L + sl;
+    const int s = s_lo + m * (kDecWaves * R::L) + sl;
     if (s >= s_hi) break;  // uniform
     u32x4_t af[J];
 #pragma unroll
@@ -313,7 +354,8 @@ __device__ __forceinline__ void dec_step(const uint8_t* slot, f32x4_t (&y)[NT], 
       const uint16_t* a = c < 2 ? xp + int64_t(c) * K + k : reinterpret_cast<const uint16_t*>(zeros);
       af[j] = *reinterpret_cast<const u32x4_t*>(a);
     }
-    const float4 x4 = g4 == 0 ? xs[s] : *reinterpret_cast<const float4*>(zeros);
+    // the group's sums (hi, lo): read by every lane, used by lanes g4 = 0
+    f32x2_t xv = lds_read_f32x2(xs + s);
     const int off = sl * (G * BITS / 8) + g4 * R::LB;  // byte of the 128-byte window
 #pragma unroll
     for (int b = 0; b < NT; ++b) {
@@ -346,8 +388,10 @@ __device__ __forceinline__ void dec_step(const uint8_t* slot, f32x4_t (&y)[NT], 
                                                       0);
       }
       const float sc = mq[0], zq = mq[1] + kOff;
-      y[b][0] = fmaf(sc, fmaf(-zq, x4.x, acc[0]), y[b][0]);
-      y[b][1] = fmaf(sc, fmaf(-zq, x4.y, acc[1]), y[b][1]);
+      if (b == 0) lgkm_wait(xv);
+      const float x0 = g4 == 0 ? xv[0] : 0.0f, x1 = g4 == 0 ? xv[1] : 0.0f;
+      y[b][0] = fmaf(sc, fmaf(-zq, x0, acc[0]), y[b][0]);
+      y[b][1] = fmaf(sc, fmaf(-zq, x1, acc[1]), y[b][1]);
     }
   }
 }
@@ -365,7 +409,9 @@ struct DecStream {
   // Wait for the oldest outstanding step (the one about to be computed).
   __device__ __forceinline__ void wait_oldest() const {
     const int ahead = issued - consumed - 1;  // steps issued after it
-    if (ahead >= 4) wait_vmcnt<4 * R::PER_STEP>();
+    if (ahead >= 6) wait_vmcnt<6 * R::PER_STEP>();
+    else if (ahead == 5) wait_vmcnt<5 * R::PER_STEP>();
+    else if (ahead == 4) wait_vmcnt<4 * R::PER_STEP>();
     else if (ahead == 3) wait_vmcnt<3 * R::PER_STEP>();
     else if (ahead == 2) wait_vmcnt<2 * R::PER_STEP>();
     else if (ahead == 1) wait_vmcnt<R::PER_STEP>();
@@ -378,9 +424,9 @@ struct DecStream {
 // (wave t ranks token t; workgroup 0 publishes idx/w for the down kernel).
 // Units (slot j = t*k + i, 16-row tile) are dealt to the workgroups in a
 // fixed stride (token-major, so a workgroup restages the activation parts
-// only when the token changes); within a unit, wave w streams groups
-// [w*GP, (w+1)*GP) of K of the gate and the up tile, and the eight partial
-// sums of each row meet in LDS.
+// only when the token changes); within a unit, wave w streams the pieces
+// w, w + 8, ... of K (L groups each) of the gate and the up tile, and the
+// eight partial sums of each row meet in LDS.
 // ---------------------------------------------------------------------------
 template <int BITS, int J>
 __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
@@ -388,7 +434,9 @@ __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   __shared__ int s_e[4 * 32];
   __shared__ float s_w[4 * 32];
-  __shared__ float red[kDecWaves][2][16];
+  // partial sums of a batch of units, double-buffered: [batch parity][unit
+  // of the batch][wave][gate | up][row]
+  __shared__ float red[2][kDecUB][kDecWaves][2][16];
   __shared__ __attribute__((aligned(16))) uint32_t zeros[4];
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -399,12 +447,13 @@ __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
   float4* xs = reinterpret_cast<float4*>(dsm + kDecWaves * R::BYTES + 4 * H);  // [S]
 
   if (threadIdx.x < 4) zeros[threadIdx.x] = 0u;
-  // waves 0..T-1 rank the tokens' scores while the others stage token 0
+  // token 0's activation is loaded first and converted once the first weight
+  // loads are in flight; waves 0..T-1 rank the tokens' scores meanwhile
+  StageRegs x0;
+  stage_load(p.X, H, nullptr, 1, H, threadIdx.x, 512, x0);
   if (wv < T)
     topk_all<kDecodeMaxE / 64>(p.logits + int64_t(wv) * p.E, p.E, k, lane, s_e + wv * k,
                                s_w + wv * k);
-  else
-    stage_parts(p.X, H, nullptr, 1, H, G, xp, xs, threadIdx.x - 64 * T, 512 - 64 * T);
   __syncthreads();
   if (blockIdx.x == 0 && threadIdx.x < T * k) {
     p.idx[threadIdx.x] = s_e[threadIdx.x];
@@ -413,9 +462,8 @@ __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
 
   const int tiles = (I + 15) / 16;
   const int units = T * k * tiles;
-  const int GP = (S + kDecWaves - 1) / kDecWaves;  // groups per wave
-  const int s_lo = min(S, wv * GP), s_hi = min(S, s_lo + GP);
-  const int NS = (GP + R::L - 1) / R::L;           // steps per unit
+  const int s_lo = wv * R::L, s_hi = S;  // the wave's first group; the row's end
+  const int NS = (S + kDecWaves * R::L - 1) / (kDecWaves * R::L);  // steps per unit
   auto unit_of = [&](int j) { return int(blockIdx.x) + j * int(gridDim.x); };
   if (unit_of(0) >= units) return;
 
@@ -443,12 +491,40 @@ __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
     }
   };
   for (int d = 0; d < R::DEPTH - 1; ++d) issue_next();
+  stage_store(x0, 1, H, G, xp, xs, threadIdx.x, 512);
+  lds_barrier();
 
+  // The partial sums of up to kDecUB units wait in LDS and are added after
+  // one barrier per batch, so the waves stream through the batch's units
+  // without meeting.  Batches alternate between two buffers: batch b's sums
+  // are read (by wave 0, after barrier b) before wave 0 reaches barrier b+1,
+  // which every wave passes before writing batch b+2.
+  auto finish_batch = [&](int j_last) {
+    lds_barrier();
+    const int b = j_last / kDecUB;
+    const int nu = j_last % kDecUB + 1;
+    if (wv == 0) {
+      for (int q = lane >> 4; q < nu; q += 4) {
+        const int r = lane & 15;
+        float gs = 0.0f, us = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) {
+          gs += red[b & 1][q][w][0][r];
+          us += red[b & 1][q][w][1][r];
+        }
+        const int uq = unit_of(b * kDecUB + q);
+        const int n = (uq % tiles) * 16 + r;
+        if (n < I) p.hbuf[int64_t(uq / tiles) * I + n] = silu(gs) * us;
+      }
+    }
+  };
   int staged = 0;
-  for (int j = 0; unit_of(j) < units; ++j) {
+  int j = 0;
+  for (; unit_of(j) < units; ++j) {
     const int u = unit_of(j);
     const int slot_j = u / tiles, t = slot_j / k;
     if (t != staged) {
+      if (j % kDecUB != 0) finish_batch(j - 1);  // the batch ends with the token
       lds_barrier();  // the previous token's parts are no longer read
       stage_parts(p.X + int64_t(t) * H, H, nullptr, 1, H, G, xp, xs, threadIdx.x, 512);
       lds_barrier();
@@ -463,29 +539,19 @@ __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
     }
     // rows 0 and 1 of the tile are the two parts of the token's product
     if (g4 == 0) {
-      red[wv][0][c] = y[0][0] + y[0][1];
-      red[wv][1][c] = y[1][0] + y[1][1];
+      red[(j / kDecUB) & 1][j % kDecUB][wv][0][c] = y[0][0] + y[0][1];
+      red[(j / kDecUB) & 1][j % kDecUB][wv][1][c] = y[1][0] + y[1][1];
     }
-    lds_barrier();
-    if (wv == 0 && lane < 16) {
-      float gs = 0.0f, us = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kDecWaves; ++w) {
-        gs += red[w][0][lane];
-        us += red[w][1][lane];
-      }
-      const int n = (u % tiles) * 16 + lane;
-      if (n < I) p.hbuf[int64_t(slot_j) * I + n] = silu(gs) * us;
-    }
-    lds_barrier();
+    if (j % kDecUB == kDecUB - 1) finish_batch(j);
   }
+  if (j % kDecUB != 0) finish_batch(j - 1);
 }
 
 // ---------------------------------------------------------------------------
 // down + combine: Y[t][n] = sum_i w[t][i] (h[t*k+i] . Wd_{idx[t][i]}[n]).
 // Units (token t, 16-row tile of H) are dealt in a fixed stride; a workgroup
-// stages the token's k activation parts, wave w streams groups [w*GP,
-// (w+1)*GP) of I of each slot's tile in slot order, weights each slot's
+// stages the token's k activation parts, wave w streams the pieces w, w + 8,
+// ... of I (L groups each) of each slot's tile in slot order, weights each slot's
 // partial sum by w[t][i], and the eight waves' sums meet in LDS in a fixed
 // order.
 // ---------------------------------------------------------------------------
@@ -506,6 +572,12 @@ __global__ __launch_bounds__(512) void dec_down_kernel(DecArgs p, int T) {
   uint16_t* hp = reinterpret_cast<uint16_t*>(dsm + kDecWaves * R::BYTES);     // [k][2][I]
   float4* hs = reinterpret_cast<float4*>(dsm + kDecWaves * R::BYTES + int64_t(k) * 4 * I);
   if (threadIdx.x < 4) zeros[threadIdx.x] = 0u;
+  // the first token's activations and the routing are loaded together; the
+  // activations are converted once the first weight loads are in flight
+  const int t_first = int(blockIdx.x) / ((H + 15) / 16);
+  StageRegs h0;  // rows t_first*k .. + k of hbuf are consecutive
+  stage_load(p.hbuf + int64_t(min(t_first, T - 1)) * k * I, I, nullptr, k, I, threadIdx.x, 512,
+             h0);
   if (threadIdx.x < T * k) {
     s_e[threadIdx.x] = p.idx[threadIdx.x];
     s_w[threadIdx.x] = p.w[threadIdx.x];
@@ -514,9 +586,8 @@ __global__ __launch_bounds__(512) void dec_down_kernel(DecArgs p, int T) {
 
   const int tiles = (H + 15) / 16;
   const int units = T * tiles;
-  const int GP = (S + kDecWaves - 1) / kDecWaves;
-  const int s_lo = min(S, wv * GP), s_hi = min(S, s_lo + GP);
-  const int NS = (GP + R::L - 1) / R::L;  // steps per slot
+  const int s_lo = wv * R::L, s_hi = S;  // the wave's first group; the row's end
+  const int NS = (S + kDecWaves * R::L - 1) / (kDecWaves * R::L);  // steps per slot
   auto unit_of = [&](int j) { return int(blockIdx.x) + j * int(gridDim.x); };
   if (unit_of(0) >= units) return;
 
@@ -547,8 +618,10 @@ __global__ __launch_bounds__(512) void dec_down_kernel(DecArgs p, int T) {
     }
   };
   for (int d = 0; d < R::DEPTH - 1; ++d) issue_next();
+  stage_store(h0, k, I, G, hp, hs, threadIdx.x, 512);
+  lds_barrier();
 
-  int staged = -1;
+  int staged = t_first;
   for (int j = 0; unit_of(j) < units; ++j) {
     const int u = unit_of(j);
     const int t = u / tiles;
@@ -619,12 +692,16 @@ hipError_t go_decode(const DecArgs& a, int64_t T, hipStream_t stream) {
 bool decode_supported(int bits, int64_t H, int64_t I, int32_t E, int32_t k) {
   if (bits != 4 && bits != 8) return false;
   // largest rings over the supported groupings (at most 4 groups per step)
-  const int64_t gu_ring = int64_t(kDecWaves) * 3 * (2 * 2048 + 2 * 16 * 4 * 8);
-  const int64_t dn_ring = int64_t(kDecWaves) * 3 * (2048 + 16 * 4 * 8);
+  constexpr int64_t kGuSlot = 2 * 2048 + 2 * 16 * 4 * 8, kDnSlot = 2048 + 16 * 4 * 8;
+  const int64_t gu_ring = int64_t(kDecWaves) * DSQ_DEC_GU_DEPTH * kGuSlot;
+  const int64_t dn_ring = int64_t(kDecWaves) * DSQ_DEC_DN_DEPTH * kDnSlot;
   const int64_t gu = gu_ring + 4 * H + (H / 64) * 16;
   const int64_t dn = dn_ring + int64_t(k) * (4 * I + (I / 64) * 16);
-  const int64_t budget = 156 * 1024;  // 160 KiB less the static tables
-  return E <= kDecodeMaxE && k <= 32 && gu <= budget && dn <= budget;
+  // 160 KiB less each kernel's static tables
+  const int64_t gu_static = int64_t(sizeof(float)) * 2 * kDecUB * kDecWaves * 2 * 16 + 2048;
+  const int64_t dn_static = 2048;
+  return E <= kDecodeMaxE && k <= 32 && gu <= 160 * 1024 - gu_static &&
+         dn <= 160 * 1024 - dn_static && stage_one_pass(1, H, 512) && stage_one_pass(k, I, 512);
 }
 
 hipError_t launch_moe_decode(const dsq_qweight& gate, const dsq_qweight& up,

@@ -77,6 +77,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 // clobber keeps the compiler from moving LDS accesses across it; unlike
 // __syncthreads() it does not wait for the wave's outstanding global loads,
 // which are the prefetches this kernel keeps in flight.
+// 8-byte LDS read the compiler's wait analysis does not see.  Once a direct
+// global->LDS load is outstanding, the compiler puts a full vmcnt(0) wait in
+// front of LDS reads it cannot prove disjoint from every such load, which
+// would drain a ring's lookahead; reads whose data a stream's own explicit
+// wait already covers go through here.  The value may be used only after
+// lgkm_wait(v), which waits for the read and, by taking v as an operand,
+// keeps every use of v behind the wait.
+__device__ __forceinline__ f32x2_t lds_read_f32x2(const void* p) {
+  f32x2_t v;
+  asm volatile("ds_read_b64 %0, %1" : "=v"(v) : "v"(uint32_t(size_t((lds_ptr_t)p))) : "memory");
+  return v;
+}
+__device__ __forceinline__ void lgkm_wait(f32x2_t& v) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v) : : "memory");
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
