@@ -173,11 +173,14 @@ struct GmmArgs {
 __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 template <int BITS, int J, bool SWIGLU>
+#ifndef DSQ_GMM_DM
+#define DSQ_GMM_DM 3
+#endif
 struct GmmShape {
   static constexpr int W = 8;                       // waves per workgroup
   static constexpr int NB = 2;                      // B tiles (16 rows) per wave
   static constexpr int L = 1024 / (J * 32 * BITS);  // groups per 128 code bytes of a row
-  static constexpr int DM = 3;                      // ring depth in steps of L groups
+  static constexpr int DM = DSQ_GMM_DM;             // ring depth in steps of L groups
   static constexpr int CSLOT = NB * 16 * 128;       // one step of a wave's codes
   static constexpr int MSLOT = NB * 16 * L * 8;     // one step of a wave's (scale, zp)
   static constexpr int PPR = L >= 2 ? L / 2 : 2;    // direct-load pieces per metadata row
@@ -215,15 +218,23 @@ __device__ __forceinline__ int gmm_item(int j) {
   return (j * 8 + b % 8) * per + b / 8;
 }
 
+// The routing tables are read through the constant address space: with a
+// workgroup-uniform index these become scalar loads, which do not queue behind
+// the weight stream's outstanding vector loads (a vector load here would wait
+// for the whole lookahead to land).  The tables are written before the kernel
+// starts and never during it.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
 template <int XP>
 __device__ __forceinline__ void gmm_cursor_load(const GmmArgs& p, int items, GmmCursor& cu) {
   cu.item = gmm_item(cu.j);
   if (cu.item >= items) return;
   const int a = cu.item / p.rt;
   if (p.active) {
-    cu.e = p.active[a];
-    cu.p0 = p.offsets[cu.e];
-    cu.M = p.offsets[cu.e + 1] - cu.p0;
+    cu.e = __builtin_amdgcn_readfirstlane(((const_i32_ptr)p.active)[a]);
+    const const_i32_ptr off = (const_i32_ptr)p.offsets;
+    cu.p0 = __builtin_amdgcn_readfirstlane(off[cu.e]);
+    cu.M = __builtin_amdgcn_readfirstlane(off[cu.e + 1]) - cu.p0;
     cu.tb = int(cu.p0 * XP / 16) + a;
   } else {
     cu.e = p.expert;
@@ -264,7 +275,8 @@ __device__ __forceinline__ void gmm_stream(const GmmArgs& p, uint8_t* sm) {
   constexpr int TPT = 16 / XP;  // tokens per tile
   constexpr int LB = J * BITS;  // code bytes per lane, tile and group
   constexpr float kOff = BITS == 4 ? 16.0f : 0.0f;
-  static_assert(DM == 3, "slot arithmetic below");
+  static_assert(DM >= 2 && DM <= 4, "waits below");
+  constexpr int A = DM - 1;  // steps issued ahead of the one computed
   const int lane = threadIdx.x & 63;
   const int c = lane & 15, g4 = lane >> 4;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -429,24 +441,30 @@ __device__ __forceinline__ void gmm_stream(const GmmArgs& p, uint8_t* sm) {
     }
   };
 
-  // steps issued so far; step g + 1 is in flight at step g iff issued > g + 1
+  // steps issued so far; at step g the steps g + 1 .. issued - 1 are in
+  // flight (at most A - 1 of them when the wait comes)
   int issued = 0;
   issue(0);
   ++issued;
-  if (la.item < items) {
-    issue(1);
-    ++issued;
+#pragma unroll
+  for (int d = 1; d < A; ++d) {
+    if (la.item < items) {
+      issue(d);
+      ++issued;
+    }
   }
   for (int g0 = 0;; g0 += DM) {
 #pragma unroll
     for (int u = 0; u < DM; ++u) {
       const int g = g0 + u;
       if (g >= issued) return;  // every issued step has been computed
-      if (issued > g + 1) wait_vmcnt<Sh::PER_STEP>();
+      const int ahead = issued - g - 1;
+      if (A >= 3 && ahead >= 2) wait_vmcnt<2 * Sh::PER_STEP>();
+      else if (A >= 2 && ahead == 1) wait_vmcnt<Sh::PER_STEP>();
       else wait_vmcnt<0>();
       lds_barrier();  // all waves' loads of step g landed; step g - 1 consumed
       if (la.item < items) {
-        issue((u + 2) % DM);
+        issue((u + A) % DM);
         ++issued;
       }
       compute(cu.m, u);
