@@ -71,6 +71,8 @@ def lib():
         L.orc_route.restype = i32
         L.orc_group.argtypes = [vp, i64, i32, i32, vp, vp, vp]
         L.orc_group.restype = i32
+        L.orc_topk_f32.argtypes = [vp, i64, i32, vp, vp]
+        L.orc_topk_f32.restype = i32
         L.orc_expert_f64.argtypes = [vp, i64, i64] + [vp] * 9 + [i32, i32] + [vp] * 6
         L.orc_moe_f32.argtypes = ([vp, i64, i64, i64, i32, i32, vp, vp] + [vp] * 9
                                   + [i32, i32, i32, vp, vp, vp])
@@ -199,6 +201,17 @@ def route(logits: np.ndarray, k: int):
     if lib().orc_route(_p(L), T, E, k, _p(idx), _p(w), _p(gap)) != 0:
         raise ValueError("orc_route: invalid arguments or non-finite logits")
     return idx, w, gap
+
+
+def topk(y: np.ndarray, k: int):
+    """Output-head selection: the k largest of y (fp32) by (value desc, index
+    asc), NaN last; returns (idx int32 [k], values float32 [k])."""
+    y = np.ascontiguousarray(y, np.float32).reshape(-1)
+    idx = np.empty((k,), np.int32)
+    val = np.empty((k,), np.float32)
+    if lib().orc_topk_f32(_p(y), y.size, k, _p(idx), _p(val)) != 0:
+        raise ValueError("orc_topk_f32: invalid arguments")
+    return idx, val
 
 
 def group(idx: np.ndarray, E: int):

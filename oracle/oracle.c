@@ -537,3 +537,42 @@ int32_t orc_moe_f32(const float* X, int64_t T, int64_t H, int64_t I, int32_t E, 
   free(perm);
   return 0;
 }
+
+/*
+ * Output-head selection: the last projection's logits choose the next token
+ * ([P1] §2.1, the pipeline ends in the output projection, logits and
+ * sampling; [P2] the session API's argmax / sample step; [P3] the end-to-end
+ * check compares the argmax at every position).  Returns the k largest of
+ * y[0..N) in rank order:
+ *   larger value first; equal values (-0 equals +0) -> smaller index first,
+ *   the first maximum a plain "if (y[i] > best)" scan keeps; NaN ranks below
+ *   every number (and among NaNs the smaller index first).
+ * Plain k-pass selection, O(k N).  Returns -1 for invalid arguments.
+ */
+static int orc_head_before(float a, int64_t ia, float b, int64_t ib) {
+  const int an = a != a, bn = b != b;
+  if (an || bn) {
+    if (an && bn) return ia < ib;
+    return bn;  /* a number ranks before a NaN */
+  }
+  if (a != b) return a > b;
+  return ia < ib;
+}
+
+int32_t orc_topk_f32(const float* y, int64_t N, int32_t k, int32_t* idx, float* val) {
+  if (!y || !idx || !val || N < 1 || k < 1 || k > N) return -1;
+  unsigned char* taken = (unsigned char*)calloc((size_t)N, 1);
+  if (!taken) return -1;
+  for (int32_t r = 0; r < k; ++r) {
+    int64_t best = -1;
+    for (int64_t i = 0; i < N; ++i) {
+      if (taken[i]) continue;
+      if (best < 0 || orc_head_before(y[i], i, y[best], best)) best = i;
+    }
+    taken[best] = 1;
+    idx[r] = (int32_t)best;
+    val[r] = y[best];
+  }
+  free(taken);
+  return 0;
+}
