@@ -101,7 +101,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cases", default="gemv8,gemv4,moe1,moe32,gemm256,moe256",
+    ap.add_argument("--cases", default="head,gemv8,gemv4,moe1,moe32,gemm256,moe256",
                     help="secondary workloads to run (comma list)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -202,8 +202,25 @@ def main():
     del W4
     torch.cuda.empty_cache()
 
+    head = []
+    if not args.no_secondary and "head" in args.cases.split(","):
+        # the output head: the same vocab GEMV followed by the top-k selection
+        # over its 129280 logits (graph-replayed, like the roofline series)
+        for k in (1, 50):
+            hidx = torch.empty(k, dtype=torch.int32, device=dev)
+            hval = torch.empty(k, device=dev)
+            hws = torch.empty(dsq.topk_workspace_bytes(NV, k) + 256, dtype=torch.uint8, device=dev)
+            hms = time_calls(lambda i: dsq.gemv_topk(WV, x, k, y=yv, idx=hidx, values=hval,
+                                                     workspace=hws), 20, 2, torch)
+            gbs = bytesv / (hms * 1e-3) / 1e9
+            head.append({"workload": f"output head: INT8 g64 vocab GEMV 4096x129280 + top-{k} "
+                                     "of the logits", "us": round(hms * 1e3, 2),
+                         "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "selection_us": round((hms - vocab_ms) * 1e3, 2)})
+            log(head[-1])
     if not args.no_secondary and args.cases:
-        result["secondary"] = secondary(dsq, synth, torch, np, dev, set(args.cases.split(",")), x)
+        result["secondary"] = head + secondary(dsq, synth, torch, np, dev,
+                                               set(args.cases.split(",")), x)
     del WV
     torch.cuda.empty_cache()
 

@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsq.so")
 SOURCES = ["api.hip", "pack.hip", "gemv.hip", "decode.hip", "route.hip",
            "gemm_mfma.hip",
-           "gmm.hip"]
+           "gmm.hip", "head.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -254,6 +254,46 @@ dsq_status dsq_moe_route_topk(const float* logits, const float* bias, int64_t T,
   return hip_status(launch_topk(logits, bias, T, E, top_k, idx, weights, (hipStream_t)stream));
 }
 
+size_t dsq_topk_workspace_bytes(int64_t N, int32_t k) {
+  if (N <= 0 || N > INT32_MAX || k <= 0 || k > N || k > kHeadMaxK) return 0;
+  return head_workspace(N, k);
+}
+
+dsq_status dsq_topk(const float* y, int64_t N, int32_t k, int32_t* idx, float* values,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!y || !idx || !values) return DSQ_ERR_INVALID_ARG;
+  if (N <= 0 || k <= 0 || k > N) return DSQ_ERR_SHAPE;
+  if (N > INT32_MAX || k > kHeadMaxK) return DSQ_ERR_UNSUPPORTED;
+  if (!aligned(y, 4) || !aligned(idx, 4) || !aligned(values, 4)) return DSQ_ERR_ALIGN;
+  const size_t need = head_workspace(N, k);
+  if (!workspace || workspace_bytes < need) return DSQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return DSQ_ERR_ALIGN;
+  dsq_status s = check_device();
+  if (s != DSQ_OK) return s;
+  return hip_status(launch_head(y, N, k, idx, values, workspace, (hipStream_t)stream));
+}
+
+dsq_status dsq_gemv_topk(const dsq_qweight* W, int64_t expert, const float* x, float* y,
+                         int32_t k, int32_t* idx, float* values, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  dsq_status s = check_qweight(W);
+  if (s != DSQ_OK) return s;
+  if (!x || !y || !idx || !values) return DSQ_ERR_INVALID_ARG;
+  if (expert < 0 || expert >= W->batch) return DSQ_ERR_INVALID_ARG;
+  if (k <= 0 || k > W->N) return DSQ_ERR_SHAPE;
+  if (W->N > INT32_MAX || k > kHeadMaxK) return DSQ_ERR_UNSUPPORTED;
+  if (!aligned(x, 16) || !aligned(y, 4) || !aligned(idx, 4) || !aligned(values, 4))
+    return DSQ_ERR_ALIGN;
+  const size_t need = head_workspace(W->N, k);
+  if (!workspace || workspace_bytes < need) return DSQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return DSQ_ERR_ALIGN;
+  if ((s = check_device()) != DSQ_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_gemv(*W, expert, x, y, st);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(launch_head(y, W->N, k, idx, values, workspace, st));
+}
+
 size_t dsq_moe_workspace_bytes(int64_t T, int32_t E, int32_t top_k, int64_t H, int64_t I,
                                int32_t math) {
   if (T < 0 || E <= 0 || top_k <= 0 || top_k > E || H <= 0 || I <= 0) return 0;

@@ -1,0 +1,239 @@
+// head.hip -- output-head selection: the k largest of N logits.
+//
+// The last projection's logits choose the next token ("Hand-writing a
+// DeepSeek inference engine in pure C", hnwysp.cn/news/134870, §2.1; "ds4
+// code walkthrough", the session API's argmax / sample step), and the
+// end-to-end check compares the argmax at every position ("Running a
+// 284B-parameter LLM from 3.2 GB of RAM in plain C").  Rank order: larger
+// value first, equal values (-0 equals +0) to the smaller index, NaN below
+// every number.
+//
+// Every value becomes one 64-bit key that orders exactly like that rule:
+//   high word: the float's bits mapped to an unsigned integer of the same
+//              order (negative values complemented, positive ones with the
+//              top bit set), both zeros mapped alike, NaN mapped to 0;
+//   low word : the complemented index, so the smaller index ranks higher.
+// Keys are distinct, and 0 (the padding) ranks below every real value.
+//
+// Selection by rounds: a workgroup keeps the best k keys of its chunk; the
+// kept keys are the next round's input, until one chunk remains, whose best
+// k are the answer (the top k of all values lie among every chunk's top k).
+// For small k a workgroup takes the block maximum of a 4096-key chunk k times
+// (the pick is removed by the one lane that holds it); for larger k it sorts
+// a 1024-key chunk in LDS with a bitonic network.
+#include "common.h"
+#include "internal.h"
+#include "mfma_util.h"
+
+namespace dsq {
+
+constexpr int kHeadChunk = 1024;      // bitonic path (k > kHeadPickMaxK)
+constexpr int kHeadSortThreads = kHeadChunk / 2;  // one pair per thread and step
+constexpr int kHeadThreads = 256;     // pick path
+constexpr int kHeadWaves = kHeadThreads / 64;
+#ifndef DSQ_HEAD_PICK_MAXK
+#define DSQ_HEAD_PICK_MAXK 16
+#endif
+constexpr int kHeadPickMaxK = DSQ_HEAD_PICK_MAXK;
+constexpr int kHeadPickPer = 16;      // keys per thread, pick path
+constexpr int kHeadPickChunk = kHeadThreads * kHeadPickPer;
+
+__device__ __forceinline__ uint64_t head_key(float v, uint32_t i) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t h;
+  if (v != v) {
+    h = 0u;
+  } else {
+    if (v == 0.0f) u = 0u;  // -0 ranks with +0
+    h = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  }
+  return (uint64_t(h) << 32) | uint64_t(~i);
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// One step of a wave maximum: each lane compares with the lane the DPP
+// control names (lanes without a source, or in rows outside ROW_MASK, keep
+// their own key).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t max_step(uint64_t v) {
+  const int lo = int(uint32_t(v)), hi = int(uint32_t(v >> 32));
+  const uint32_t olo = uint32_t(__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false));
+  const uint32_t ohi = uint32_t(__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false));
+  return umax64(v, (uint64_t(ohi) << 32) | olo);
+}
+
+// The largest key of the wave, in every lane: row shifts leave each row's
+// maximum in its lane 15, the two row broadcasts carry them to lane 63.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  v = max_step<0x111, 0xf>(v);  // row_shr:1
+  v = max_step<0x112, 0xf>(v);  // row_shr:2
+  v = max_step<0x114, 0xf>(v);  // row_shr:4
+  v = max_step<0x118, 0xf>(v);  // row_shr:8
+  v = max_step<0x142, 0xa>(v);  // row_bcast:15
+  v = max_step<0x143, 0xc>(v);  // row_bcast:31
+  const uint32_t lo = __builtin_amdgcn_readlane(int(uint32_t(v)), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 63);
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// Write the r-th best key of a round: FINAL as (index, value), else as a key
+// of the next round's input.
+template <bool FINAL>
+__device__ __forceinline__ void head_emit(uint64_t key, int r, const float* __restrict__ y,
+                                          uint64_t* __restrict__ out, int32_t* __restrict__ idx,
+                                          float* __restrict__ val, int k) {
+  if (FINAL) {
+    const uint32_t i = ~uint32_t(key);
+    idx[r] = int32_t(i);
+    val[r] = y[i];
+  } else {
+    out[int64_t(blockIdx.x) * k + r] = key;
+  }
+}
+
+// One round, bitonic path.  FROM_Y: the input is the logits (keys are formed
+// here), else the previous round's keys.  FINAL (one workgroup): write the k
+// best as (index, value); else write them as keys to out[block][k].
+template <bool FROM_Y, bool FINAL>
+__global__ __launch_bounds__(kHeadSortThreads) void head_round_kernel(const float* __restrict__ y,
+                                                                      const uint64_t* __restrict__ in,
+                                                                      int64_t n, int k,
+                                                                      uint64_t* __restrict__ out,
+                                                                      int32_t* __restrict__ idx,
+                                                                      float* __restrict__ val) {
+  __shared__ uint64_t s[kHeadChunk];
+  const int64_t base = int64_t(blockIdx.x) * kHeadChunk;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = threadIdx.x + h * kHeadSortThreads;
+    const int64_t i = base + j;
+    uint64_t key = 0;
+    if (i < n) key = FROM_Y ? head_key(y[i], uint32_t(i)) : in[i];
+    s[j] = key;
+  }
+  lds_barrier();
+  // bitonic network: blocks of `size` alternate direction, the last one
+  // (size = 1024) sorts the chunk descending; thread t owns the pair
+  // (lo, lo + stride) of every step.  (Steps of stride <= 64 stay inside a
+  // wave's own 128 keys and could skip the barrier, but measured slower.)
+  const int t = threadIdx.x;
+  for (int size = 2; size <= kHeadChunk; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const int lo = 2 * t - (t & (stride - 1));
+      const bool desc = (lo & size) == 0;
+      const uint64_t a = s[lo], b = s[lo + stride];
+      if ((a < b) == desc) {
+        s[lo] = b;
+        s[lo + stride] = a;
+      }
+      lds_barrier();
+    }
+  }
+  for (int r = t; r < k; r += kHeadSortThreads) head_emit<FINAL>(s[r], r, y, out, idx, val, k);
+}
+
+// One round, pick path: k times the block maximum of the workgroup's chunk.
+// Each thread holds kHeadPickPer keys (strided by the block size, so a wave's
+// loads are contiguous) and keeps their maximum; a pick is the wave maxima's
+// maximum, and the one thread that holds it clears that key and recomputes
+// its maximum.  The wave maxima alternate between two LDS slots, so one
+// barrier per pick suffices: a wave writes slot r & 1 again only after every
+// wave has passed the barrier of pick r + 1, which it reaches after reading
+// the slot for pick r.  The picks are kept in LDS and written after the loop.
+template <bool FROM_Y, bool FINAL>
+__global__ __launch_bounds__(kHeadThreads) void head_pick_kernel(const float* __restrict__ y,
+                                                                 const uint64_t* __restrict__ in,
+                                                                 int64_t n, int k,
+                                                                 uint64_t* __restrict__ out,
+                                                                 int32_t* __restrict__ idx,
+                                                                 float* __restrict__ val) {
+  __shared__ uint64_t wmax[2][kHeadWaves];
+  __shared__ uint64_t picked[kHeadPickMaxK > 0 ? kHeadPickMaxK : 1];
+  const int64_t base = int64_t(blockIdx.x) * kHeadPickChunk;
+  uint64_t v[kHeadPickPer];
+#pragma unroll
+  for (int q = 0; q < kHeadPickPer; ++q) {
+    const int64_t i = base + threadIdx.x + int64_t(q) * kHeadThreads;
+    uint64_t key = 0;
+    if (i < n) key = FROM_Y ? head_key(y[i], uint32_t(i)) : in[i];
+    v[q] = key;
+  }
+  uint64_t lm = v[0];
+#pragma unroll
+  for (int q = 1; q < kHeadPickPer; ++q) lm = umax64(lm, v[q]);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int r = 0; r < k; ++r) {
+    const uint64_t b = wave_max_key(lm);
+    if (lane == 0) wmax[r & 1][wv] = b;
+    lds_barrier();
+    uint64_t m = wmax[r & 1][0];
+#pragma unroll
+    for (int w = 1; w < kHeadWaves; ++w) m = umax64(m, wmax[r & 1][w]);
+    // real keys are distinct, so one thread owns m (when only padding is
+    // left m is 0, and clearing zeros changes nothing)
+    if (lm == m) {
+      uint64_t nm = 0;
+#pragma unroll
+      for (int q = 0; q < kHeadPickPer; ++q) {
+        v[q] = v[q] == m ? 0 : v[q];
+        nm = umax64(nm, v[q]);
+      }
+      lm = nm;
+    }
+    if (threadIdx.x == 0) picked[r] = m;
+  }
+  lds_barrier();
+  for (int r = threadIdx.x; r < k; r += kHeadThreads) head_emit<FINAL>(picked[r], r, y, out, idx, val, k);
+}
+
+namespace {
+
+int64_t chunk_of(int32_t k) { return k <= kHeadPickMaxK ? kHeadPickChunk : kHeadChunk; }
+int64_t chunks(int64_t n, int32_t k) { return (n + chunk_of(k) - 1) / chunk_of(k); }
+
+template <bool FROM_Y, bool FINAL>
+void launch_round(int64_t nb, const float* y, const uint64_t* in, int64_t n, int32_t k,
+                  uint64_t* out, int32_t* idx, float* val, hipStream_t stream) {
+  if (k <= kHeadPickMaxK)
+    hipLaunchKernelGGL((head_pick_kernel<FROM_Y, FINAL>), dim3(unsigned(nb)), dim3(kHeadThreads),
+                       0, stream, y, in, n, k, out, idx, val);
+  else
+    hipLaunchKernelGGL((head_round_kernel<FROM_Y, FINAL>), dim3(unsigned(nb)),
+                       dim3(kHeadSortThreads), 0, stream, y, in, n, k, out, idx, val);
+}
+
+}  // namespace
+
+size_t head_workspace(int64_t N, int32_t k) {
+  if (chunks(N, k) == 1) return 256;  // no intermediate keys; nonzero means supported
+  // two ping-pong key buffers, each large enough for the first round's output
+  return size_t(2) * align256(chunks(N, k) * k * 8);
+}
+
+hipError_t launch_head(const float* y, int64_t N, int32_t k, int32_t* idx, float* val,
+                       void* workspace, hipStream_t stream) {
+  const int64_t half = chunks(N, k) == 1 ? 0 : align256(chunks(N, k) * k * 8);
+  uint64_t* buf[2] = {static_cast<uint64_t*>(workspace),
+                      reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) + half)};
+  int64_t n = N;
+  int round = 0;
+  while (true) {
+    const int64_t nb = chunks(n, k);
+    const uint64_t* in = round == 0 ? nullptr : buf[(round - 1) & 1];
+    if (nb == 1) {
+      if (round == 0) launch_round<true, true>(1, y, in, n, k, nullptr, idx, val, stream);
+      else launch_round<false, true>(1, y, in, n, k, nullptr, idx, val, stream);
+      return hipGetLastError();
+    }
+    uint64_t* out = buf[round & 1];
+    if (round == 0) launch_round<true, false>(nb, y, in, n, k, out, nullptr, nullptr, stream);
+    else launch_round<false, false>(nb, y, in, n, k, out, nullptr, nullptr, stream);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    n = nb * k;
+    ++round;
+  }
+}
+
+}  // namespace dsq

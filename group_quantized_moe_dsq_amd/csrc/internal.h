@@ -81,4 +81,11 @@ hipError_t launch_gmm(const dsq_qweight& A, const dsq_qweight* B, int64_t expert
                       int xp, void* act, size_t act_bytes, float* xs, size_t xs_bytes,
                       float* out, int64_t ld_out, hipStream_t stream);
 
+// Output-head selection: the k (<= kHeadMaxK) largest of N logits in rank
+// order (head.hip).  Workspace: head_workspace(N, k) bytes.
+constexpr int32_t kHeadMaxK = 256;
+size_t head_workspace(int64_t N, int32_t k);
+hipError_t launch_head(const float* y, int64_t N, int32_t k, int32_t* idx, float* val,
+                       void* workspace, hipStream_t stream);
+
 }  // namespace dsq

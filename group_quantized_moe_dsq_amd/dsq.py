@@ -25,7 +25,8 @@ LAYOUT_VERSION = 1
 
 EXPORTS = ["dsq_status_string", "dsq_packed_bytes", "dsq_qweight_init", "dsq_pack_weights",
            "dsq_gemv", "dsq_gemm_workspace_bytes", "dsq_gemm", "dsq_moe_route_topk",
-           "dsq_moe_workspace_bytes", "dsq_moe_ffn"]
+           "dsq_moe_workspace_bytes", "dsq_moe_ffn", "dsq_topk_workspace_bytes", "dsq_topk",
+           "dsq_gemv_topk"]
 
 
 class DsqError(RuntimeError):
@@ -75,6 +76,12 @@ def lib():
         L.dsq_moe_ffn.argtypes = [vp, vp, vp, pd, pd, pd, i64, i32, i32, vp, vp, sz, vp, vp, vp,
                                   vp, vp]
         L.dsq_moe_ffn.restype = i32
+        L.dsq_topk_workspace_bytes.argtypes = [i64, i32]
+        L.dsq_topk_workspace_bytes.restype = sz
+        L.dsq_topk.argtypes = [vp, i64, i32, vp, vp, vp, sz, vp]
+        L.dsq_topk.restype = i32
+        L.dsq_gemv_topk.argtypes = [pd, i64, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.dsq_gemv_topk.restype = i32
         _lib = L
     return _lib
 
@@ -152,6 +159,51 @@ def gemv(W: QWeight, x: torch.Tensor, y: torch.Tensor | None = None, expert: int
     _check(lib().dsq_gemv(ctypes.byref(W.desc), expert, _ptr(x), _ptr(y), _stream(stream)),
            "dsq_gemv")
     return y
+
+
+def topk_workspace_bytes(N: int, k: int) -> int:
+    return int(lib().dsq_topk_workspace_bytes(N, k))
+
+
+def _workspace(workspace, need, device):
+    if workspace is None and need:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=device)
+    if workspace is None:
+        return None, 0
+    off = (-workspace.data_ptr()) % 256
+    return ctypes.c_void_p(workspace.data_ptr() + off), workspace.numel() - off
+
+
+def topk(y: torch.Tensor, k: int, idx=None, values=None, workspace=None, stream=None):
+    """The k largest of y in rank order (value desc, smaller index on ties,
+    NaN last): returns (idx int32 [k], values fp32 [k])."""
+    _need(y, torch.float32, "y")
+    N = y.numel()
+    if idx is None:
+        idx = torch.empty(k, dtype=torch.int32, device=y.device)
+    if values is None:
+        values = torch.empty(k, dtype=torch.float32, device=y.device)
+    wptr, wbytes = _workspace(workspace, topk_workspace_bytes(N, k), y.device)
+    _check(lib().dsq_topk(_ptr(y), N, k, _ptr(idx), _ptr(values), wptr, wbytes,
+                          _stream(stream)), "dsq_topk")
+    return idx, values
+
+
+def gemv_topk(W: QWeight, x: torch.Tensor, k: int, y: torch.Tensor | None = None, expert: int = 0,
+              idx=None, values=None, workspace=None, stream=None):
+    """Output head: y = W[expert] x, then the k largest of y; returns
+    (y, idx, values)."""
+    _need(x, torch.float32, "x")
+    if y is None:
+        y = torch.empty(W.N, dtype=torch.float32, device=x.device)
+    if idx is None:
+        idx = torch.empty(k, dtype=torch.int32, device=x.device)
+    if values is None:
+        values = torch.empty(k, dtype=torch.float32, device=x.device)
+    wptr, wbytes = _workspace(workspace, topk_workspace_bytes(W.N, k), x.device)
+    _check(lib().dsq_gemv_topk(ctypes.byref(W.desc), expert, _ptr(x), _ptr(y), k, _ptr(idx),
+                               _ptr(values), wptr, wbytes, _stream(stream)), "dsq_gemv_topk")
+    return y, idx, values
 
 
 def gemm_workspace_bytes(M: int, N: int, K: int, math: int) -> int:

@@ -188,6 +188,40 @@ dsq_status dsq_moe_route_topk(const float* logits, const float* bias, int64_t T,
                               int32_t top_k, int32_t* idx, float* weights, void* stream);
 
 /*
+ * dsq_topk -- output-head selection: the k largest logits, which choose the
+ * next token (hnwysp.cn/news/134870 §2.1: the pipeline ends in the output
+ * projection, logits and sampling; "ds4 code walkthrough": the session
+ * API's argmax / sample step; "Running a 284B-parameter LLM from 3.2 GB of
+ * RAM in plain C": the end-to-end check compares the argmax at every
+ * position).
+ *   y      : fp32 [N] device, read only.
+ *   idx    : int32 [k] device: the k largest in rank order -- larger value
+ *            first; equal values (-0 equals +0) rank the smaller index
+ *            first (the first maximum a greater-than scan keeps); NaN ranks
+ *            below every number.  k = 1 is the argmax.
+ *   values : fp32 [k] device: y[idx[r]].
+ *   workspace : dsq_topk_workspace_bytes(N, k) bytes, 256-byte aligned
+ *            (contents on entry ignored).
+ * Exact: the selection compares the fp32 values themselves.
+ * Limits: 1 <= k <= min(N, 256), N < 2^31.  Errors: DSQ_ERR_INVALID_ARG,
+ * DSQ_ERR_SHAPE (k out of 1..N), DSQ_ERR_UNSUPPORTED (k > 256),
+ * DSQ_ERR_ALIGN, DSQ_ERR_WORKSPACE, DSQ_ERR_NO_DEVICE, DSQ_ERR_HIP.
+ */
+size_t dsq_topk_workspace_bytes(int64_t N, int32_t k);
+dsq_status dsq_topk(const float* y, int64_t N, int32_t k, int32_t* idx, float* values,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dsq_gemv_topk -- the output head: y = dequant(W[expert]) x (as dsq_gemv,
+ * written to y) followed by dsq_topk(y, W->N, k, ...) on the same stream.
+ * Arguments, limits and errors as the two calls; workspace:
+ * dsq_topk_workspace_bytes(W->N, k).
+ */
+dsq_status dsq_gemv_topk(const dsq_qweight* W, int64_t expert, const float* x, float* y,
+                         int32_t k, int32_t* idx, float* values, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/*
  * dsq_moe_ffn -- one routed MoE layer:
  *   l = X Wr^T (+ bias)                    router logits, fp32
  *   (idx, w) = route_topk(l)               as dsq_moe_route_topk

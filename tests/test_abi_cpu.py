@@ -149,3 +149,31 @@ def test_layout_decoder_round_trip():
             word0 = raw[0:4]
             assert [int(b) & 15 for b in word0] == list(codes[0, 0:4])
             assert [int(b) >> 4 for b in word0] == list(codes[0, 4:8])
+
+
+def test_topk_validation_and_workspace_query():
+    L = dsq.lib()
+    fake = ctypes.c_void_p(0x60000)
+    mis = ctypes.c_void_p(0x60002)
+    N = 129280
+    need = dsq.topk_workspace_bytes(N, 50)
+    # two ping-pong buffers of the first round's kept keys: k <= 64 keeps 50
+    # keys per 4096-value chunk (32 chunks), larger k per 1024-value chunk
+    assert need >= 2 * 32 * 50 * 8 and need % 256 == 0
+    assert dsq.topk_workspace_bytes(N, 200) >= 2 * 127 * 200 * 8
+    assert dsq.topk_workspace_bytes(1000, 5) > 0          # one chunk: no keys kept
+    assert dsq.topk_workspace_bytes(N, 0) == 0
+    assert dsq.topk_workspace_bytes(10, 11) == 0
+    assert dsq.topk_workspace_bytes(N, 257) == 0
+    ws = ctypes.c_void_p(0x80000)
+    assert L.dsq_topk(None, N, 1, fake, fake, ws, need, None) == -1
+    assert L.dsq_topk(fake, N, 0, fake, fake, ws, need, None) == -2
+    assert L.dsq_topk(fake, 10, 11, fake, fake, ws, need, None) == -2
+    assert L.dsq_topk(fake, N, 257, fake, fake, ws, need, None) == -5
+    assert L.dsq_topk(mis, N, 1, fake, fake, ws, need, None) == -3
+    assert L.dsq_topk(fake, N, 50, fake, fake, ws, need - 1, None) == -4
+    assert L.dsq_topk(fake, N, 50, fake, fake, None, need, None) == -4
+    d, _ = desc(8, 64, 256, 100, 1)
+    assert L.dsq_gemv_topk(ctypes.byref(d), 0, fake, fake, 101, fake, fake, ws, 1 << 20, None) == -2
+    assert L.dsq_gemv_topk(ctypes.byref(d), 1, fake, fake, 1, fake, fake, ws, 1 << 20, None) == -1
+    assert L.dsq_gemv_topk(ctypes.byref(d), 0, mis, fake, 1, fake, fake, ws, 1 << 20, None) == -3
