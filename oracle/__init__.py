@@ -9,7 +9,8 @@ The arithmetic lives in ``oracle.c`` (plain C99 + OpenMP, built with
 composes the per-expert reference into a whole MoE layer.
 
 Sources: "Hand-writing a DeepSeek inference engine in pure C"
-(hnwysp.cn/news/134870) §2.3, §3.2-§3.5, §5.1; "Running a 284B-parameter LLM
+(hnwysp.cn/news/134870) §2.1, §2.3, §3.2-§3.5, §5.1; "ds4 code walkthrough"
+(the RMSNorm epsilon); "Running a 284B-parameter LLM
 from 3.2 GB of RAM in plain C" (feinterview.poetries.top), section on bitwise
 identical CPU paths.
 
@@ -73,6 +74,8 @@ def lib():
         L.orc_group.restype = i32
         L.orc_topk_f32.argtypes = [vp, i64, i32, vp, vp]
         L.orc_topk_f32.restype = i32
+        L.orc_rmsnorm_f64.argtypes = [vp, vp, i64, i64, ctypes.c_double, vp]
+        L.orc_rmsnorm_f64.restype = i32
         L.orc_expert_f64.argtypes = [vp, i64, i64] + [vp] * 9 + [i32, i32] + [vp] * 6
         L.orc_moe_f32.argtypes = ([vp, i64, i64, i64, i32, i32, vp, vp] + [vp] * 9
                                   + [i32, i32, i32, vp, vp, vp])
@@ -201,6 +204,20 @@ def route(logits: np.ndarray, k: int):
     if lib().orc_route(_p(L), T, E, k, _p(idx), _p(w), _p(gap)) != 0:
         raise ValueError("orc_route: invalid arguments or non-finite logits")
     return idx, w, gap
+
+
+def rmsnorm_f64(X: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of each row of X (fp32 [T][H]) with weight g (fp32 [H]) and
+    epsilon eps, in fp64: x / sqrt(mean(x^2) + eps) * g."""
+    X = np.ascontiguousarray(X, np.float32)
+    X2 = X.reshape(-1, X.shape[-1])
+    g = np.ascontiguousarray(g, np.float32).reshape(-1)
+    if g.size != X2.shape[1]:
+        raise ValueError("rmsnorm_f64: weight length differs from the row length")
+    out = np.empty(X2.shape, np.float64)
+    if lib().orc_rmsnorm_f64(_p(X2), _p(g), X2.shape[0], X2.shape[1], float(eps), _p(out)) != 0:
+        raise ValueError("orc_rmsnorm_f64: invalid arguments")
+    return out.reshape(X.shape)
 
 
 def topk(y: np.ndarray, k: int):

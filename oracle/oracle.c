@@ -25,13 +25,16 @@
  *        §3.5  MoE router = linear layer + softmax + top-k (partial sort of
  *              (score, index) pairs, greater-first), tokens grouped per expert,
  *              weighted sum of the expert outputs;
- *        §5.1/§5.3  a zero scale is an error (assert scale != 0).
+ *        §5.1/§5.3  a zero scale is an error (assert scale != 0);
+ *        §2.1  each block normalises with RMSNorm before its FFN / MoE step
+ *              and adds the residual after it.
+ *   [P2] "ds4 code walkthrough": the RMSNorm epsilon constant (1e-6).
  *   [P3] "Running a 284B-parameter LLM from 3.2 GB of RAM in plain C"
  *        (feinterview.poetries.top): the scalar and OpenMP CPU paths must be
  *        bitwise identical (fixed accumulator tree, no fp contraction).
  *
- * Readings where the pages are silent or garbled are listed in the design doc and
- * restated next to the code that takes them.
+ * Where the pages are silent or garbled, the reading taken is stated next to
+ * the code that takes it.
  */
 #include <float.h>
 #include <math.h>
@@ -574,5 +577,27 @@ int32_t orc_topk_f32(const float* y, int64_t N, int32_t k, int32_t* idx, float* 
     val[r] = y[best];
   }
   free(taken);
+  return 0;
+}
+
+/*
+ * RMSNorm of each row, the normalisation a block applies before its FFN
+ * ("Hand-writing a DeepSeek inference engine in pure C", §2.1: every block
+ * normalises with RMSNorm before the feed-forward / MoE step and adds the
+ * residual after it; "ds4 code walkthrough", the model constants: epsilon
+ * 1e-6).  The formula is the standard one, which the pages name but do not
+ * print: out[t][h] = x[t][h] / sqrt(mean_h x[t][h]^2 + eps) * g[h], all in
+ * double.  Returns -1 for invalid arguments.
+ */
+int32_t orc_rmsnorm_f64(const float* x, const float* g, int64_t T, int64_t H, double eps,
+                        double* out) {
+  if (!x || !g || !out || T < 0 || H < 1 || !(eps >= 0.0)) return -1;
+  for (int64_t t = 0; t < T; ++t) {
+    const float* row = x + t * H;
+    double ss = 0.0;
+    for (int64_t h = 0; h < H; ++h) ss += (double)row[h] * (double)row[h];
+    const double rms = sqrt(ss / (double)H + eps);
+    for (int64_t h = 0; h < H; ++h) out[t * H + h] = (double)row[h] / rms * (double)g[h];
+  }
   return 0;
 }
