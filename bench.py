@@ -101,7 +101,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cases", default="head,gemv8,gemv4,moe1,moe32,gemm256,moe256",
+    ap.add_argument("--cases", default="head,gemv8,gemv4,moe1,block1,moe32,gemm256,moe256",
                     help="secondary workloads to run (comma list)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -273,23 +273,29 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
         torch.cuda.synchronize()
         return router, bias, g, u, d
 
-    def moe_case(name, layer, T, nsets, math, bits, group, iters):
+    def moe_case(name, layer, T, nsets, math, bits, group, iters, block=False):
+        # block: the MoE step with its RMSNorm and residual (dsq_moe_block)
         H = 4096
         Xs = [synth.normal((T, H), 1.0, 0, synth.X, 1000 + T * 100 + s, device=dev)
               for s in range(nsets)]
-        ws = torch.empty(dsq.moe_workspace_bytes(T, 256, 6, H, 2048, math) + 256,
-                         dtype=torch.uint8, device=dev)
+        gamma = synth.normal((H,), 0.25, 0, synth.X, 900, device=dev) + 1.0
+        wsq = dsq.moe_block_workspace_bytes if block else dsq.moe_workspace_bytes
+        ws = torch.empty(wsq(T, 256, 6, H, 2048, math) + 256, dtype=torch.uint8, device=dev)
         Y = torch.empty((T, H), device=dev)
         counts = torch.empty(256, dtype=torch.int32, device=dev)
+
+        def run(X, **kw):
+            if block:
+                return dsq.moe_block(layer, X, gamma, 1e-6, math=math, Y=Y, workspace=ws, **kw)
+            return dsq.moe_ffn(layer, X, math=math, Y=Y, workspace=ws, **kw)
         touched = []
         for s in range(nsets):
-            dsq.moe_ffn(layer, Xs[s], math=math, Y=Y, workspace=ws, counts_out=counts)
+            run(Xs[s], counts_out=counts)
             touched.append(int((counts > 0).sum().item()))
         D = float(np.mean(touched))
-        ms = time_calls(lambda i: dsq.moe_ffn(layer, Xs[i % nsets], math=math, Y=Y,
-                                              workspace=ws), iters, 4, torch)
+        ms = time_calls(lambda i: run(Xs[i % nsets]), iters, 4, torch)
         eb = 3 * qbytes(bits, group, H, 2048)
-        b = 256 * H * 4 + D * eb + 2 * T * H * 4
+        b = 256 * H * 4 + D * eb + 2 * T * H * 4 + (H * 4 if block else 0)
         flops = 2 * T * 256 * H + 2 * T * 6 * 3 * H * 2048
         gbs = b / (ms * 1e-3) / 1e9
         rec = {"workload": name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
@@ -298,11 +304,15 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
         out.append(rec)
         log(rec)
 
-    if "moe1" in cases or "moe32" in cases:
+    if "moe1" in cases or "moe32" in cases or "block1" in cases:
         r, b, g, u, d = build_moe(4, 64, None)
         if "moe1" in cases:
             moe_case("MoE decode T=1, 256 experts top-6, INT4 g64 SwiGLU",
                      dsq.MoeLayer(r, g, u, d, None, 6), 1, 64, dsq.MATH_FP32, 4, 64, 64)
+        if "block1" in cases:
+            moe_case("MoE block decode T=1 (RMSNorm + MoE + residual), INT4 g64 SwiGLU",
+                     dsq.MoeLayer(r, g, u, d, None, 6), 1, 64, dsq.MATH_FP32, 4, 64, 64,
+                     block=True)
         if "moe32" in cases:
             bias = synth.normal((256,), 1.0, 0, synth.BIAS, 0, device=dev)
             moe_case("MoE batched decode T=32 skewed (router bias ~N(0,1)), INT4 g64",

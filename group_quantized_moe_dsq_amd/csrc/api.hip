@@ -5,6 +5,7 @@
 // returns a status instead of exiting, allocates nothing (callers pass
 // workspace; the same walkthrough forbids allocation in the token loop) and
 // only enqueues kernels on the caller's stream.
+#include <float.h>
 #include <string.h>
 
 #include "common.h"
@@ -306,11 +307,16 @@ size_t dsq_moe_workspace_bytes(int64_t T, int32_t E, int32_t top_k, int64_t H, i
   return ovf ? 0 : size_t(n);
 }
 
-dsq_status dsq_moe_ffn(const float* X, const float* router_w, const float* bias,
-                       const dsq_qweight* gate, const dsq_qweight* up, const dsq_qweight* down,
-                       int64_t T, int32_t top_k, int32_t math, float* Y, void* workspace,
-                       size_t workspace_bytes, float* logits_out, int32_t* idx_out,
-                       float* w_out, int32_t* expert_counts_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shape and type rules shared by the MoE layer and the MoE block.
+dsq_status check_moe(const float* X, const float* router_w, const float* bias,
+                     const dsq_qweight* gate, const dsq_qweight* up, const dsq_qweight* down,
+                     int64_t T, int32_t top_k, int32_t math, const float* Y,
+                     const float* logits_out, const int32_t* idx_out, const float* w_out,
+                     const int32_t* expert_counts_out) {
   if (!X || !router_w || !Y) return DSQ_ERR_INVALID_ARG;
   dsq_status s;
   if ((s = check_qweight(gate)) != DSQ_OK) return s;
@@ -327,47 +333,53 @@ dsq_status dsq_moe_ffn(const float* X, const float* router_w, const float* bias,
     return DSQ_ERR_SHAPE;
   if (T < 0 || top_k <= 0 || top_k > E64) return DSQ_ERR_SHAPE;
   if (T > 65536 || E64 > 4096 || top_k > 32) return DSQ_ERR_UNSUPPORTED;
-  const int32_t E = int32_t(E64);
   if (!aligned(X, 16) || !aligned(router_w, 16) || !aligned(Y, 16) || (bias && !aligned(bias, 4)))
     return DSQ_ERR_ALIGN;
   if ((logits_out && !aligned(logits_out, 4)) || (idx_out && !aligned(idx_out, 4)) ||
       (w_out && !aligned(w_out, 4)) || (expert_counts_out && !aligned(expert_counts_out, 4)))
     return DSQ_ERR_ALIGN;
-  const bool bf16 = use_bf16(math, T);
-  const size_t need = dsq_moe_workspace_bytes(T, E, top_k, H, I, math);
-  if (need == 0) return DSQ_ERR_OVERFLOW;
-  if (!workspace || workspace_bytes < need) return DSQ_ERR_WORKSPACE;
-  if (!aligned(workspace, 256)) return DSQ_ERR_ALIGN;
-  if (T == 0) return DSQ_OK;
-  if ((s = check_device()) != DSQ_OK) return s;
+  return DSQ_OK;
+}
 
+// The MoE layer of the pages (§3.5) on the rows X.  With gamma the rows are
+// RMS-normalised into xn first and the experts see xn (§2.1: RMSNorm before
+// the MoE step); with resid the residual is added to Y.
+dsq_status run_moe(const float* X, const float* gamma, float eps, float* xn, const float* resid,
+                   const float* router_w, const float* bias, const dsq_qweight& gate,
+                   const dsq_qweight& up, const dsq_qweight& down, int64_t T, int32_t top_k,
+                   bool bf16, float* Y, void* workspace, float* logits_out, int32_t* idx_out,
+                   float* w_out, int32_t* expert_counts_out, hipStream_t st) {
+  const int32_t E = int32_t(gate.batch);
+  const int64_t E64 = gate.batch, H = gate.K, I = gate.N;
   MoeWs m{};
   moe_layout(workspace, T, E, top_k, H, I, 64, bf16, &m, nullptr);
   if (logits_out) m.logits = logits_out;
   if (idx_out) m.idx = idx_out;
   if (w_out) m.w = w_out;
   if (expert_counts_out) m.counts = expert_counts_out;
-  hipStream_t st = (hipStream_t)stream;
+  // the rows the experts (and a separate router) read
+  const float* Xe = gamma ? xn : X;
   hipError_t e;
 #define DSQ_TRY(call)                          \
   if ((e = (call)) != hipSuccess) return hip_status(e);
-  if (!bf16 && T <= kDecodeMaxTokens && decode_supported(gate->bits, H, I, E, top_k)) {
+  if (!bf16 && T <= kDecodeMaxTokens && decode_supported(gate.bits, H, I, E, top_k)) {
     // Decode: every (token, slot) pair is its own GEMV; no grouping needed.
     // The gate/up kernel ranks the scores itself and publishes idx/w.
-    DSQ_TRY(launch_router_gemv(X, T, router_w, bias, E, H, m.logits, st));
-    DSQ_TRY(launch_moe_decode(*gate, *up, *down, X, T, E, top_k, m.logits, m.idx, m.w,
-                              static_cast<float*>(m.hbuf), Y, st));
+    DSQ_TRY(launch_router_gemv(X, T, router_w, bias, E, H, m.logits, gamma, eps, xn, st));
+    DSQ_TRY(launch_moe_decode(gate, up, down, Xe, T, E, top_k, m.logits, m.idx, m.w,
+                              static_cast<float*>(m.hbuf), Y, resid, st));
     if (expert_counts_out) {
       DSQ_TRY(launch_group(m.idx, T, top_k, E, m.bitmap, m.counts, m.offsets, m.perm, m.pos,
                            m.active, m.n_active, st));
     }
     return DSQ_OK;
   }
-  // (1) router logits, fp32, bias included
+  // (0) + (1) normalisation and router logits, fp32, bias included
   if (T <= 32) {
-    DSQ_TRY(launch_router_gemv(X, T, router_w, bias, E, H, m.logits, st));
+    DSQ_TRY(launch_router_gemv(X, T, router_w, bias, E, H, m.logits, gamma, eps, xn, st));
   } else {
-    DSQ_TRY(launch_router(X, T, router_w, bias, E, H, m.logits, st));
+    if (gamma) DSQ_TRY(launch_rmsnorm(X, gamma, T, H, eps, xn, st));
+    DSQ_TRY(launch_router(Xe, T, router_w, bias, E, H, m.logits, st));
   }
   // (2) softmax + top-k + renormalisation
   DSQ_TRY(launch_topk(m.logits, nullptr, T, E, top_k, m.idx, m.w, st));
@@ -382,16 +394,74 @@ dsq_status dsq_moe_ffn(const float* X, const float* router_w, const float* bias,
   g.top_k = top_k;
   const int64_t max_items = T * top_k < E64 ? T * top_k : E64;
   g.max_items = int32_t(max_items);
-  // (4) expert FFNs over their token groups, (5) weighted combine
+  // (4) expert FFNs over their token groups, (5) weighted combine (+ residual)
   const int xp = bf16 ? 1 : 2;
   float* hbuf = static_cast<float*>(m.hbuf);
-  DSQ_TRY(launch_gmm(*gate, up, 0, &g, XR_GATHER, X, H, 0, xp, m.act, m.act_bytes, m.xs,
+  DSQ_TRY(launch_gmm(gate, &up, 0, &g, XR_GATHER, Xe, H, 0, xp, m.act, m.act_bytes, m.xs,
                      m.xs_bytes, hbuf, I, st));
-  DSQ_TRY(launch_gmm(*down, nullptr, 0, &g, XR_SEGMENT, hbuf, I, 0, xp, m.act, m.act_bytes, m.xs,
+  DSQ_TRY(launch_gmm(down, nullptr, 0, &g, XR_SEGMENT, hbuf, I, 0, xp, m.act, m.act_bytes, m.xs,
                      m.xs_bytes, m.ybuf, H, st));
-  DSQ_TRY(launch_combine(m.ybuf, m.pos, m.w, T, top_k, H, Y, st));
+  DSQ_TRY(launch_combine(m.ybuf, m.pos, m.w, T, top_k, H, resid, Y, st));
 #undef DSQ_TRY
   return DSQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsq_status dsq_moe_ffn(const float* X, const float* router_w, const float* bias,
+                       const dsq_qweight* gate, const dsq_qweight* up, const dsq_qweight* down,
+                       int64_t T, int32_t top_k, int32_t math, float* Y, void* workspace,
+                       size_t workspace_bytes, float* logits_out, int32_t* idx_out,
+                       float* w_out, int32_t* expert_counts_out, void* stream) {
+  dsq_status s = check_moe(X, router_w, bias, gate, up, down, T, top_k, math, Y, logits_out,
+                           idx_out, w_out, expert_counts_out);
+  if (s != DSQ_OK) return s;
+  const size_t need =
+      dsq_moe_workspace_bytes(T, int32_t(gate->batch), top_k, gate->K, gate->N, math);
+  if (need == 0) return DSQ_ERR_OVERFLOW;
+  if (!workspace || workspace_bytes < need) return DSQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return DSQ_ERR_ALIGN;
+  if (T == 0) return DSQ_OK;
+  if ((s = check_device()) != DSQ_OK) return s;
+  return run_moe(X, nullptr, 0.0f, nullptr, nullptr, router_w, bias, *gate, *up, *down, T, top_k,
+                 use_bf16(math, T), Y, workspace, logits_out, idx_out, w_out, expert_counts_out,
+                 (hipStream_t)stream);
+}
+
+size_t dsq_moe_block_workspace_bytes(int64_t T, int32_t E, int32_t top_k, int64_t H, int64_t I,
+                                     int32_t math) {
+  const size_t moe = dsq_moe_workspace_bytes(T, E, top_k, H, I, math);
+  if (moe == 0) return 0;
+  // the normalised rows come first
+  return size_t(align256(T * H * 4)) + moe;
+}
+
+dsq_status dsq_moe_block(const float* X, const float* norm_w, float eps, const float* router_w,
+                         const float* bias, const dsq_qweight* gate, const dsq_qweight* up,
+                         const dsq_qweight* down, int64_t T, int32_t top_k, int32_t math,
+                         float* Y, void* workspace, size_t workspace_bytes, float* xn_out,
+                         float* logits_out, int32_t* idx_out, float* w_out,
+                         int32_t* expert_counts_out, void* stream) {
+  dsq_status s = check_moe(X, router_w, bias, gate, up, down, T, top_k, math, Y, logits_out,
+                           idx_out, w_out, expert_counts_out);
+  if (s != DSQ_OK) return s;
+  if (!norm_w) return DSQ_ERR_INVALID_ARG;
+  if (!(eps > 0.0f) || !(eps <= FLT_MAX)) return DSQ_ERR_INVALID_ARG;  // rejects NaN too
+  if (!aligned(norm_w, 16) || (xn_out && !aligned(xn_out, 16))) return DSQ_ERR_ALIGN;
+  const size_t need =
+      dsq_moe_block_workspace_bytes(T, int32_t(gate->batch), top_k, gate->K, gate->N, math);
+  if (need == 0) return DSQ_ERR_OVERFLOW;
+  if (!workspace || workspace_bytes < need) return DSQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return DSQ_ERR_ALIGN;
+  if (T == 0) return DSQ_OK;
+  if ((s = check_device()) != DSQ_OK) return s;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* xn = xn_out ? xn_out : reinterpret_cast<float*>(ws);
+  return run_moe(X, norm_w, eps, xn, X, router_w, bias, *gate, *up, *down, T, top_k,
+                 use_bf16(math, T), Y, ws + align256(T * gate->K * 4), logits_out, idx_out, w_out,
+                 expert_counts_out, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -31,13 +31,23 @@ namespace dsq {
 // (expert, tile of TT tokens); its 256 threads split K (float4 granularity),
 // so the 16 KiB row is read by 256 lanes at once; per-wave partials meet in
 // LDS and are added in a fixed order.
+//
+// With gamma the rows are first normalised (RMSNorm before the MoE step,
+// "Hand-writing a DeepSeek inference engine in pure C" §2.1):
+// xn = (x * r) * gamma, r = 1 / sqrt(mean(x^2) + eps).  Every workgroup
+// computes r itself from the whole row (same code, same order, so the same
+// bits everywhere), and the expert-0 workgroup of each token tile writes xn
+// for the later kernels.
 // ---------------------------------------------------------------------------
 template <int TT>
 __global__ __launch_bounds__(256) void router_gemv_kernel(const float* __restrict__ X, int T,
                                                           const float* __restrict__ Wr,
                                                           const float* __restrict__ bias, int E,
-                                                          int H, float* __restrict__ logits) {
+                                                          int H, float* __restrict__ logits,
+                                                          const float* __restrict__ gamma,
+                                                          float eps, float* __restrict__ xn) {
   __shared__ float red[4][TT];
+  __shared__ float red_ss[4][TT];
   const int e = blockIdx.x;
   const int t0 = blockIdx.y * TT;
   const int tt = min(TT, T - t0);
@@ -45,6 +55,38 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const float* __restric
   const int n4 = H / 4;
   const float4* w4 = reinterpret_cast<const float4*>(Wr + int64_t(e) * H);
   const float4* x4 = reinterpret_cast<const float4*>(X + int64_t(t0) * H);
+  const float4* g4 = reinterpret_cast<const float4*>(gamma);
+  float4* xn4 = reinterpret_cast<float4*>(xn + int64_t(t0) * H);
+  const bool write_xn = xn != nullptr && e == 0;
+  float rinv[TT];
+  if (gamma) {
+    float ss[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) ss[t] = 0.0f;
+    for (int j0 = threadIdx.x; j0 < n4; j0 += 1024) {
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        const int tc = min(t, tt - 1);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float4 v = x4[int64_t(tc) * n4 + min(j0 + 256 * u, n4 - 1)];
+          const bool keep = t < tt && j0 + 256 * u < n4;
+          ss[t] = fmaf(v.x, keep ? v.x : 0.0f, ss[t]);
+          ss[t] = fmaf(v.y, keep ? v.y : 0.0f, ss[t]);
+          ss[t] = fmaf(v.z, keep ? v.z : 0.0f, ss[t]);
+          ss[t] = fmaf(v.w, keep ? v.w : 0.0f, ss[t]);
+        }
+      }
+    }
+    const float s = wave_reduce_scatter<TT>(ss);
+    if ((lane & (64 / TT - 1)) == 0) red_ss[wv][reduce_scatter_row<TT>(lane)] = s;
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      const float tot = ((red_ss[0][t] + red_ss[1][t]) + red_ss[2][t]) + red_ss[3][t];
+      rinv[t] = 1.0f / sqrtf(tot / float(H) + eps);
+    }
+  }
   float acc[TT];
 #pragma unroll
   for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
@@ -52,15 +94,29 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const float* __restric
   // Loads from clamped addresses (no branches, all in flight at once); a
   // duplicated weight float4 is paired with a zeroed x float4.
   for (int j0 = threadIdx.x; j0 < n4; j0 += 1024) {
-    float4 w[4];
+    float4 w[4], gv[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) w[u] = w4[min(j0 + 256 * u, n4 - 1)];
+    if (gamma) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) gv[u] = g4[min(j0 + 256 * u, n4 - 1)];
+    }
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       const int tc = min(t, tt - 1);
       float4 xv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) xv[u] = x4[int64_t(tc) * n4 + min(j0 + 256 * u, n4 - 1)];
+      if (gamma) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          xv[u].x = (xv[u].x * rinv[t]) * gv[u].x;
+          xv[u].y = (xv[u].y * rinv[t]) * gv[u].y;
+          xv[u].z = (xv[u].z * rinv[t]) * gv[u].z;
+          xv[u].w = (xv[u].w * rinv[t]) * gv[u].w;
+          if (write_xn && t < tt && j0 + 256 * u < n4) xn4[int64_t(t) * n4 + j0 + 256 * u] = xv[u];
+        }
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const bool keep = t < tt && j0 + 256 * u < n4;
@@ -83,19 +139,20 @@ __global__ __launch_bounds__(256) void router_gemv_kernel(const float* __restric
 }
 
 hipError_t launch_router_gemv(const float* X, int64_t T, const float* Wr, const float* bias,
-                              int32_t E, int64_t H, float* logits, hipStream_t stream) {
+                              int32_t E, int64_t H, float* logits, const float* gamma, float eps,
+                              float* xn, hipStream_t stream) {
   if (T <= 1) {
     hipLaunchKernelGGL(router_gemv_kernel<1>, dim3(E, unsigned(T)), dim3(256), 0, stream, X,
-                       int(T), Wr, bias, E, int(H), logits);
+                       int(T), Wr, bias, E, int(H), logits, gamma, eps, xn);
   } else if (T <= 2) {
     hipLaunchKernelGGL(router_gemv_kernel<2>, dim3(E, 1), dim3(256), 0, stream, X, int(T), Wr,
-                       bias, E, int(H), logits);
+                       bias, E, int(H), logits, gamma, eps, xn);
   } else if (T <= 4) {
     hipLaunchKernelGGL(router_gemv_kernel<4>, dim3(E, 1), dim3(256), 0, stream, X, int(T), Wr,
-                       bias, E, int(H), logits);
+                       bias, E, int(H), logits, gamma, eps, xn);
   } else {
     hipLaunchKernelGGL(router_gemv_kernel<8>, dim3(E, unsigned((T + 7) / 8)), dim3(256), 0,
-                       stream, X, int(T), Wr, bias, E, int(H), logits);
+                       stream, X, int(T), Wr, bias, E, int(H), logits, gamma, eps, xn);
   }
   return hipGetLastError();
 }
@@ -113,6 +170,7 @@ struct DecArgs {
   float* w;              // [T][k] written by the gate/up kernel
   float* hbuf;           // [T*k][I]
   float* Y;              // [T][H]
+  const float* resid;    // [T][H] added to Y, or NULL (may equal Y)
 };
 
 #ifndef DSQ_DEC_GU_DEPTH
@@ -652,7 +710,12 @@ __global__ __launch_bounds__(512) void dec_down_kernel(DecArgs p, int T) {
 #pragma unroll
       for (int w = 0; w < kDecWaves; ++w) v += red[w][lane];
       const int nn = (u % tiles) * 16 + lane;
-      if (nn < H) p.Y[int64_t(t) * H + nn] = v;
+      if (nn < H) {
+        // the residual is read and Y written by the same lane, so Y may be
+        // the residual itself
+        if (p.resid) v = p.resid[int64_t(t) * H + nn] + v;
+        p.Y[int64_t(t) * H + nn] = v;
+      }
     }
     lds_barrier();
   }
@@ -707,7 +770,7 @@ bool decode_supported(int bits, int64_t H, int64_t I, int32_t E, int32_t k) {
 hipError_t launch_moe_decode(const dsq_qweight& gate, const dsq_qweight& up,
                              const dsq_qweight& down, const float* X, int64_t T, int32_t E,
                              int32_t k, const float* logits, int32_t* idx, float* w, float* hbuf,
-                             float* Y, hipStream_t stream) {
+                             float* Y, const float* resid, hipStream_t stream) {
   const Layout Lgu = layout_of(gate.bits, gate.group, gate.K, gate.N);
   const Layout Ld = layout_of(down.bits, down.group, down.K, down.N);
   DecArgs a{};
@@ -729,6 +792,7 @@ hipError_t launch_moe_decode(const dsq_qweight& gate, const dsq_qweight& up,
   a.w = w;
   a.hbuf = hbuf;
   a.Y = Y;
+  a.resid = resid;
   const bool g64 = gate.group == 64;
   if (gate.bits == 8) return g64 ? go_decode<8, 2>(a, T, stream) : go_decode<8, 4>(a, T, stream);
   return g64 ? go_decode<4, 2>(a, T, stream) : go_decode<4, 4>(a, T, stream);

@@ -42,22 +42,30 @@ hipError_t launch_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, uin
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
                         int32_t* active, int32_t* n_active, hipStream_t stream);
 
-// Y[t][n] = sum_i w[t][i] * ybuf[pos[t*k+i]][n]
+// Y[t][n] = (resid[t][n] +) sum_i w[t][i] * ybuf[pos[t*k+i]][n]; Y may be resid
 hipError_t launch_combine(const float* ybuf, const int32_t* pos, const float* w, int64_t T,
-                          int32_t k, int64_t H, float* Y, hipStream_t stream);
+                          int32_t k, int64_t H, const float* resid, float* Y,
+                          hipStream_t stream);
+
+// xn[t] = X[t] / sqrt(mean(X[t]^2) + eps) * gamma, one workgroup per row
+hipError_t launch_rmsnorm(const float* X, const float* gamma, int64_t T, int64_t H, float eps,
+                          float* xn, hipStream_t stream);
 
 // Decode path (few tokens): fp32 router GEMV, and the expert FFN per routing
 // slot on the matrix cores (gate/up + SwiGLU into hbuf [T*k][I], then down
 // fused with the weighted combine into Y).
+// With gamma, the rows are RMS-normalised first and the normalised rows are
+// written to xn (when xn is not NULL).
 hipError_t launch_router_gemv(const float* X, int64_t T, const float* Wr, const float* bias,
-                              int32_t E, int64_t H, float* logits, hipStream_t stream);
+                              int32_t E, int64_t H, float* logits, const float* gamma, float eps,
+                              float* xn, hipStream_t stream);
 constexpr int64_t kDecodeMaxTokens = 4;  // decode kernels: at most this many tokens
 bool decode_supported(int bits, int64_t H, int64_t I, int32_t E, int32_t k);
 // Ranks each token's scores itself (writing idx/w), so no separate top-k.
 hipError_t launch_moe_decode(const dsq_qweight& gate, const dsq_qweight& up,
                              const dsq_qweight& down, const float* X, int64_t T, int32_t E,
                              int32_t k, const float* logits, int32_t* idx, float* w, float* hbuf,
-                             float* Y, hipStream_t stream);
+                             float* Y, const float* resid, hipStream_t stream);
 
 // bf16 MFMA dense GEMM (prefill): the workspace holds the fp32 partial
 // tiles when the K range is split.  Supported while X and one weight entry

@@ -321,12 +321,15 @@ hipError_t launch_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, uin
 }
 
 // ---------------------------------------------------------------------------
-// Weighted combine in slot order (§3.5: weighted sum of the expert outputs).
+// Weighted combine in slot order (§3.5: weighted sum of the expert outputs),
+// plus the block's residual when `resid` is given (§2.1: the residual is
+// added after the MoE step).  The residual element is read and Y written by
+// the same thread, so Y may be the residual itself.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf,
                                                       const int32_t* __restrict__ pos,
                                                       const float* __restrict__ w, int T, int k,
-                                                      int H, float* __restrict__ Y) {
+                                                      int H, const float* resid, float* Y) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;  // float4 index
   const int h4 = H / 4;
   if (i >= int64_t(T) * h4) return;
@@ -340,15 +343,65 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     acc.z = fmaf(ws, v.z, acc.z);
     acc.w = fmaf(ws, v.w, acc.w);
   }
+  if (resid) {
+    const float4 r = reinterpret_cast<const float4*>(resid + int64_t(t) * H)[c];
+    acc.x = r.x + acc.x;
+    acc.y = r.y + acc.y;
+    acc.z = r.z + acc.z;
+    acc.w = r.w + acc.w;
+  }
   reinterpret_cast<float4*>(Y + int64_t(t) * H)[c] = acc;
 }
 
 hipError_t launch_combine(const float* ybuf, const int32_t* pos, const float* w, int64_t T,
-                          int32_t k, int64_t H, float* Y, hipStream_t stream) {
+                          int32_t k, int64_t H, const float* resid, float* Y,
+                          hipStream_t stream) {
   const int64_t n = T * (H / 4);
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(combine_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, ybuf,
-                     pos, w, int(T), k, int(H), Y);
+                     pos, w, int(T), k, int(H), resid, Y);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm of each token row before the MoE step (§2.1; epsilon from the
+// model constants of "ds4 code walkthrough"): xn = (x * r) * gamma with
+// r = 1 / sqrt(mean(x^2) + eps).  One workgroup per row; each thread sums the
+// squares of its float4s in order, the waves' sums meet in LDS in a fixed
+// order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ X,
+                                                      const float* __restrict__ gamma, int H,
+                                                      float eps, float* __restrict__ xn) {
+  __shared__ float red[4];
+  const int n4 = H / 4;
+  const float4* x4 = reinterpret_cast<const float4*>(X + int64_t(blockIdx.x) * H);
+  const float4* g4 = reinterpret_cast<const float4*>(gamma);
+  float4* o4 = reinterpret_cast<float4*>(xn + int64_t(blockIdx.x) * H);
+  float ss = 0.0f;
+  for (int j = threadIdx.x; j < n4; j += 256) {
+    const float4 v = x4[j];
+    ss = fmaf(v.x, v.x, ss);
+    ss = fmaf(v.y, v.y, ss);
+    ss = fmaf(v.z, v.z, ss);
+    ss = fmaf(v.w, v.w, ss);
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = ((red[0] + red[1]) + red[2]) + red[3];
+  const float r = 1.0f / sqrtf(tot / float(H) + eps);
+  for (int j = threadIdx.x; j < n4; j += 256) {
+    const float4 v = x4[j], g = g4[j];
+    o4[j] = make_float4((v.x * r) * g.x, (v.y * r) * g.y, (v.z * r) * g.z, (v.w * r) * g.w);
+  }
+}
+
+hipError_t launch_rmsnorm(const float* X, const float* gamma, int64_t T, int64_t H, float eps,
+                          float* xn, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(unsigned(T)), dim3(256), 0, stream, X, gamma, int(H),
+                     eps, xn);
   return hipGetLastError();
 }
 

@@ -26,7 +26,7 @@ LAYOUT_VERSION = 1
 EXPORTS = ["dsq_status_string", "dsq_packed_bytes", "dsq_qweight_init", "dsq_pack_weights",
            "dsq_gemv", "dsq_gemm_workspace_bytes", "dsq_gemm", "dsq_moe_route_topk",
            "dsq_moe_workspace_bytes", "dsq_moe_ffn", "dsq_topk_workspace_bytes", "dsq_topk",
-           "dsq_gemv_topk"]
+           "dsq_gemv_topk", "dsq_moe_block_workspace_bytes", "dsq_moe_block"]
 
 
 class DsqError(RuntimeError):
@@ -76,6 +76,11 @@ def lib():
         L.dsq_moe_ffn.argtypes = [vp, vp, vp, pd, pd, pd, i64, i32, i32, vp, vp, sz, vp, vp, vp,
                                   vp, vp]
         L.dsq_moe_ffn.restype = i32
+        L.dsq_moe_block_workspace_bytes.argtypes = [i64, i32, i32, i64, i64, i32]
+        L.dsq_moe_block_workspace_bytes.restype = sz
+        L.dsq_moe_block.argtypes = [vp, vp, ctypes.c_float, vp, vp, pd, pd, pd, i64, i32, i32, vp,
+                                    vp, sz, vp, vp, vp, vp, vp, vp]
+        L.dsq_moe_block.restype = i32
         L.dsq_topk_workspace_bytes.argtypes = [i64, i32]
         L.dsq_topk_workspace_bytes.restype = sz
         L.dsq_topk.argtypes = [vp, i64, i32, vp, vp, vp, sz, vp]
@@ -273,4 +278,32 @@ def moe_ffn(layer: MoeLayer, X: torch.Tensor, math: int = MATH_AUTO, Y=None,
                              ctypes.c_void_p(workspace.data_ptr() + off),
                              workspace.numel() - off, _ptr(logits_out), _ptr(idx_out),
                              _ptr(w_out), _ptr(counts_out), _stream(stream)), "dsq_moe_ffn")
+    return Y
+
+
+def moe_block_workspace_bytes(T: int, E: int, top_k: int, H: int, I: int, math: int) -> int:
+    return int(lib().dsq_moe_block_workspace_bytes(T, E, top_k, H, I, math))
+
+
+def moe_block(layer: MoeLayer, X: torch.Tensor, norm_w: torch.Tensor, eps: float = 1e-6,
+              math: int = MATH_AUTO, Y=None, workspace: torch.Tensor | None = None, xn_out=None,
+              logits_out=None, idx_out=None, w_out=None, counts_out=None, stream=None):
+    """Y = X + moe_ffn(rmsnorm(X) * norm_w); Y may be X (in-place update)."""
+    _need(X, torch.float32, "X")
+    _need(norm_w, torch.float32, "norm_w")
+    T = X.shape[0]
+    if Y is None:
+        Y = torch.empty((T, layer.H), dtype=torch.float32, device=X.device)
+    need = moe_block_workspace_bytes(T, layer.E, layer.top_k, layer.H, layer.I, math)
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=X.device)
+    off = (-workspace.data_ptr()) % 256
+    _check(lib().dsq_moe_block(_ptr(X), _ptr(norm_w), float(eps), _ptr(layer.router_w),
+                               _ptr(layer.bias), ctypes.byref(layer.gate.desc),
+                               ctypes.byref(layer.up.desc), ctypes.byref(layer.down.desc), T,
+                               layer.top_k, math, _ptr(Y),
+                               ctypes.c_void_p(workspace.data_ptr() + off),
+                               workspace.numel() - off, _ptr(xn_out), _ptr(logits_out),
+                               _ptr(idx_out), _ptr(w_out), _ptr(counts_out), _stream(stream)),
+           "dsq_moe_block")
     return Y

@@ -254,6 +254,38 @@ dsq_status dsq_moe_ffn(const float* X, const float* router_w, const float* bias,
                        size_t workspace_bytes, float* logits_out, int32_t* idx_out,
                        float* w_out, int32_t* expert_counts_out, void* stream);
 
+/*
+ * dsq_moe_block -- the MoE step of a transformer block with its norm and
+ * residual ("Hand-writing a DeepSeek inference engine in pure C",
+ * hnwysp.cn/news/134870, §2.1: each block normalises with RMSNorm before the
+ * feed-forward / MoE step and adds the residual after it; the epsilon of the
+ * "ds4 code walkthrough" model constants is 1e-6):
+ *   xn[t] = X[t] / sqrt(mean_h X[t][h]^2 + eps) * norm_w      fp32
+ *   Y     = X + moe_ffn(xn)                                    as dsq_moe_ffn
+ *   X       : fp32 [T][H] device, the residual stream.  Y may be X itself
+ *             (in-place update); any other overlap of Y with an input is
+ *             undefined.
+ *   norm_w  : fp32 [H] device, 16-byte aligned, the RMSNorm weight.
+ *   eps     : finite, > 0 (the pages use 1e-6).
+ *   router_w, bias, gate, up, down, T, top_k, math : as dsq_moe_ffn; the
+ *             router and the experts see xn.
+ *   workspace : dsq_moe_block_workspace_bytes(T, E, top_k, H, I, math)
+ *             bytes, 256-byte aligned (contents on entry ignored).
+ *   Optional outputs (NULL to skip): xn_out fp32 [T][H] (16-byte aligned,
+ *   the normalised rows), and logits_out, idx_out, w_out, expert_counts_out
+ *   as dsq_moe_ffn.
+ * Limits as dsq_moe_ffn.  Errors as dsq_moe_ffn, plus DSQ_ERR_INVALID_ARG
+ * for a NULL norm_w or an eps that is not finite and positive.
+ */
+size_t dsq_moe_block_workspace_bytes(int64_t T, int32_t E, int32_t top_k, int64_t H, int64_t I,
+                                     int32_t math);
+dsq_status dsq_moe_block(const float* X, const float* norm_w, float eps, const float* router_w,
+                         const float* bias, const dsq_qweight* gate, const dsq_qweight* up,
+                         const dsq_qweight* down, int64_t T, int32_t top_k, int32_t math,
+                         float* Y, void* workspace, size_t workspace_bytes, float* xn_out,
+                         float* logits_out, int32_t* idx_out, float* w_out,
+                         int32_t* expert_counts_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,6 +1,7 @@
 """Helpers for the GPU parity tests: build packed weights through the C ABI,
 read them back through the independent layout reader, and compare results
 with the oracle under the bounds the tests state."""
+import itertools
 import sys
 
 import numpy as np
@@ -92,3 +93,70 @@ class MoeFixture:
             self._cache[e] = oracle.quantize_expert(g.cpu().numpy(), u.cpu().numpy(),
                                                     d.cpu().numpy(), self.bits, self.group)
         return self._cache[e]
+
+
+def check_moe_result(fx, Xin, L, idx, w, counts, k, rel, tokens=None):
+    """Checks a MoE layer's logits, routing and weights on the rows Xin (the
+    rows the layer's router and experts saw) against the oracle, and returns
+    (tokens, reference output, bound) for the output check:
+      logits : |l - l_ref| <= 1e-5 * sum_h |x_h wr_h|  (+ one fp32 rounding of
+               the bias addition);
+      idx    : the same expert set as the oracle's for every token whose
+               oracle margin between the k-th and (k+1)-th logit exceeds twice
+               the logit bound; for the others (near-ties, where both choices
+               are right) the GPU's set must be one of the sets the oracle
+               admits within that bound; slots ordered by the kernel's own
+               fp32 scores;
+      w      : first-order softmax propagation of the logit bound, + 1e-6;
+      Y      : rel * sum_i w_i (S_i + P_i) + sum_i dw_i |y_i|, with S_i the
+               down-projection magnitude sum, P_i the first-order effect of a
+               relative error rel in the gate/up sums (both from the oracle),
+               dw_i the weight bound."""
+    T = Xin.shape[0]
+    Xc = np.asarray(Xin, np.float64)
+    bias = None if fx.bias is None else fx.bias.cpu().numpy().astype(np.float64)
+    Lref, SL = oracle.router_f64(Xc, fx.router.cpu().numpy(), bias)
+    lb = 1e-5 * SL + 2.0 ** -23 * np.abs(Lref)
+    assert_bounded(L, Lref, lb, "router logits")
+
+    ref_idx, ref_w, gap = oracle.route(Lref, k)
+    delta = lb.max(axis=1)
+    clear = gap > 2 * delta
+    say(f"  routing: {int(clear.sum())}/{T} tokens with a clear top-{k} margin")
+    for t in range(T):
+        if clear[t]:
+            assert set(idx[t]) == set(ref_idx[t]), f"token {t}: top-{k} set differs"
+        else:
+            kth = np.sort(Lref[t])[::-1][k - 1]
+            certain = np.nonzero(Lref[t] > kth + 2 * delta[t])[0]
+            cand = np.nonzero(np.abs(Lref[t] - kth) <= 2 * delta[t])[0]
+            valid = [set(certain) | set(c) for c in
+                     itertools.combinations(cand, k - len(certain))]
+            assert set(idx[t]) in valid, f"token {t}: {sorted(idx[t])} is not a valid top-{k}"
+        # slot order: descending in the kernel's own fp32 scores, ties to the
+        # higher expert index
+        s = L[t, idx[t]]
+        for i in range(k - 1):
+            assert s[i] > s[i + 1] or (s[i] == s[i + 1] and idx[t, i] > idx[t, i + 1])
+    # the grouping counts are the routing histogram
+    np.testing.assert_array_equal(counts, np.bincount(idx.reshape(-1), minlength=fx.E))
+    sel_idx = idx.copy()        # validated above against the oracle's sets
+    # routing weights of the selected sets, from the oracle's logits
+    sel_l = np.take_along_axis(Lref, sel_idx.astype(np.int64), 1)
+    ex = np.exp(sel_l - sel_l.max(axis=1, keepdims=True))
+    wref = ex / ex.sum(axis=1, keepdims=True)
+    d_l = np.take_along_axis(lb, sel_idx.astype(np.int64), 1)
+    dw = wref * (d_l + (wref * d_l).sum(axis=1, keepdims=True)) + 1e-6
+    assert_bounded(w, wref, dw, "routing weights")
+
+    tokens = range(T) if tokens is None else tokens
+    H = fx.H
+    Yref = np.zeros((len(tokens), H))
+    bound = np.zeros((len(tokens), H))
+    for r, t in enumerate(tokens):
+        for i in range(k):
+            e = int(sel_idx[t, i])
+            y, Sd, Pd = oracle.expert_f64(Xc[t], fx.oracle_expert(e))
+            Yref[r] += wref[t, i] * y
+            bound[r] += rel * wref[t, i] * (Sd + Pd) + dw[t, i] * np.abs(y)
+    return np.asarray(list(tokens)), Yref, bound

@@ -131,6 +131,30 @@ def test_moe_validation_and_workspace_query():
     assert dsq.moe_workspace_bytes(5, E, 9, H, I, 0) == 0
 
 
+def test_moe_block_validation_and_workspace_query():
+    L = dsq.lib()
+    H, I, E = 256, 128, 8
+    g, _ = desc(4, 64, H, I, E)
+    u, _ = desc(4, 64, H, I, E)
+    dn, _ = desc(4, 64, I, H, E)
+    fake = ctypes.c_void_p(0x40000)
+    need = dsq.moe_block_workspace_bytes(5, E, 2, H, I, dsq.MATH_FP32)
+    # the normalised rows come first, 256-byte aligned
+    assert need == dsq.moe_workspace_bytes(5, E, 2, H, I, dsq.MATH_FP32) + 5 * H * 4
+
+    def call(norm_w, eps, ws_bytes, k=2, xn=None):
+        return L.dsq_moe_block(fake, norm_w, eps, fake, None, ctypes.byref(g), ctypes.byref(u),
+                               ctypes.byref(dn), 5, k, 0, fake, fake, ws_bytes, xn, None, None,
+                               None, None, None)
+    assert call(None, 1e-6, need) == -1                      # no norm weight
+    for eps in (0.0, -1e-6, float("nan"), float("inf")):
+        assert call(fake, eps, need) == -1, eps              # eps not finite and positive
+    assert call(fake, 1e-6, need - 1) == -4                  # workspace too small
+    assert call(fake, 1e-6, need, k=9) == -2                 # k > E
+    assert call(fake, 1e-6, need, xn=ctypes.c_void_p(0x40004)) == -3  # xn_out misaligned
+    assert dsq.moe_block_workspace_bytes(5, E, 9, H, I, 0) == 0
+
+
 def test_layout_decoder_round_trip():
     """The test-side layout reader inverts its own encoder, and the encoder
     puts INT4 codes where the header says (word j, byte i: k = 8j+i low,

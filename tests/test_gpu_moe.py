@@ -16,14 +16,12 @@ Method: "Hand-writing a DeepSeek inference engine in pure C"
            relative error rel in the gate/up sums (both from the oracle), dw_i
            the weight bound; rel = 1e-5 (fp32) or 1e-2 (bf16 MFMA).
 """
-import itertools
-
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_util import MoeFixture, assert_bounded, assert_normwise, say
+from gpu_util import MoeFixture, assert_bounded, assert_normwise, check_moe_result, say
 from group_quantized_moe_dsq_amd import dsq, synth
 
 pytestmark = pytest.mark.gpu
@@ -46,55 +44,8 @@ def run_moe(fx: MoeFixture, X, k, math):
 
 
 def check_moe(fx: MoeFixture, X, k, math, rel, tokens=None):
-    T = X.shape[0]
     Y, L, idx, w, counts = run_moe(fx, X, k, math)
-    Xc = X.cpu().numpy().astype(np.float64)
-    bias = None if fx.bias is None else fx.bias.cpu().numpy().astype(np.float64)
-    Lref, SL = oracle.router_f64(Xc, fx.router.cpu().numpy(), bias)
-    lb = 1e-5 * SL + 2.0 ** -23 * np.abs(Lref)
-    assert_bounded(L, Lref, lb, "router logits")
-
-    ref_idx, ref_w, gap = oracle.route(Lref, k)
-    delta = lb.max(axis=1)
-    clear = gap > 2 * delta
-    say(f"  routing: {int(clear.sum())}/{T} tokens with a clear top-{k} margin")
-    for t in range(T):
-        if clear[t]:
-            assert set(idx[t]) == set(ref_idx[t]), f"token {t}: top-{k} set differs"
-        else:
-            kth = np.sort(Lref[t])[::-1][k - 1]
-            certain = np.nonzero(Lref[t] > kth + 2 * delta[t])[0]
-            cand = np.nonzero(np.abs(Lref[t] - kth) <= 2 * delta[t])[0]
-            valid = [set(certain) | set(c) for c in
-                     itertools.combinations(cand, k - len(certain))]
-            assert set(idx[t]) in valid, f"token {t}: {sorted(idx[t])} is not a valid top-{k}"
-        # slot order: descending in the kernel's own fp32 scores, ties to the
-        # higher expert index
-        s = L[t, idx[t]]
-        for i in range(k - 1):
-            assert s[i] > s[i + 1] or (s[i] == s[i + 1] and idx[t, i] > idx[t, i + 1])
-    # the grouping counts are the routing histogram
-    np.testing.assert_array_equal(counts, np.bincount(idx.reshape(-1), minlength=fx.E))
-    sel_idx = idx.copy()        # validated above against the oracle's sets
-    # routing weights of the selected sets, from the oracle's logits
-    sel_l = np.take_along_axis(Lref, sel_idx.astype(np.int64), 1)
-    ex = np.exp(sel_l - sel_l.max(axis=1, keepdims=True))
-    wref = ex / ex.sum(axis=1, keepdims=True)
-    d_l = np.take_along_axis(lb, sel_idx.astype(np.int64), 1)
-    dw = wref * (d_l + (wref * d_l).sum(axis=1, keepdims=True)) + 1e-6
-    assert_bounded(w, wref, dw, "routing weights")
-
-    tokens = range(T) if tokens is None else tokens
-    H = fx.H
-    Yref = np.zeros((len(tokens), H))
-    bound = np.zeros((len(tokens), H))
-    for r, t in enumerate(tokens):
-        for i in range(k):
-            e = int(sel_idx[t, i])
-            y, Sd, Pd = oracle.expert_f64(Xc[t], fx.oracle_expert(e))
-            Yref[r] += wref[t, i] * y
-            bound[r] += rel * wref[t, i] * (Sd + Pd) + dw[t, i] * np.abs(y)
-    tok = np.asarray(list(tokens))
+    tok, Yref, bound = check_moe_result(fx, X.cpu().numpy(), L, idx, w, counts, k, rel, tokens)
     assert_bounded(Y[tok], Yref, bound, "moe output")
     if rel > 1e-5:
         assert_normwise(Y[tok], Yref, rel, "moe output")
