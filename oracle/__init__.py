@@ -76,6 +76,14 @@ def lib():
         L.orc_topk_f32.restype = i32
         L.orc_rmsnorm_f64.argtypes = [vp, vp, i64, i64, ctypes.c_double, vp]
         L.orc_rmsnorm_f64.restype = i32
+        L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+        L.orc_f32_to_f16.restype = ctypes.c_uint16
+        L.orc_f16_to_f64.argtypes = [ctypes.c_uint16]
+        L.orc_f16_to_f64.restype = ctypes.c_double
+        L.orc_sb4_quantize.argtypes = [vp, i64, i64, vp, vp]
+        L.orc_sb4_quantize.restype = i64
+        L.orc_sb4_dequant_f64.argtypes = [vp, i64, i64, vp]
+        L.orc_sb4_dequant_f64.restype = i32
         L.orc_expert_f64.argtypes = [vp, i64, i64] + [vp] * 9 + [i32, i32] + [vp] * 6
         L.orc_moe_f32.argtypes = ([vp, i64, i64, i64, i32, i32, vp, vp] + [vp] * 9
                                   + [i32, i32, i32, vp, vp, vp])
@@ -145,6 +153,54 @@ def unpack_q(m: QMat) -> np.ndarray:
     out[:, 0::2] = m.q & 0x0F
     out[:, 1::2] = m.q >> 4
     return out
+
+
+# --------------------------------------------------------------------------
+# Two-level super-block 4-bit format (see oracle.c for the reading of the
+# block's fields): blocks[rows][K/256][144] =
+#   [fp16 d][fp16 dmin][12 bytes: sc_0..7, m_0..7 as 6-bit fields][128 B codes]
+# --------------------------------------------------------------------------
+SB_K = 256
+SB_BYTES = 144
+
+
+class SB4Mat:
+    def __init__(self, blocks, flags, rows, K):
+        self.blocks, self.flags, self.rows, self.K = blocks, flags, rows, K
+
+    def dequant_f64(self) -> np.ndarray:
+        w = np.empty((self.rows, self.K), np.float64)
+        if lib().orc_sb4_dequant_f64(_p(self.blocks), self.rows, self.K, _p(w)) != 0:
+            raise ValueError("orc_sb4_dequant_f64: invalid arguments")
+        return w
+
+
+def sb4_quantize(w: np.ndarray) -> SB4Mat:
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    rows, K = w.shape
+    if K % SB_K:
+        raise ValueError("sb4_quantize: K must be a multiple of 256")
+    blocks = np.empty((rows, K // SB_K, SB_BYTES), np.uint8)
+    flags = np.empty((rows, K // SB_K), np.uint8)
+    if lib().orc_sb4_quantize(_p(w), rows, K, _p(blocks), _p(flags)) < 0:
+        raise ValueError("orc_sb4_quantize: invalid arguments")
+    return SB4Mat(blocks, flags, rows, K)
+
+
+def f16_bits(values) -> np.ndarray:
+    """fp32 -> binary16 bits (round to nearest even), one value at a time."""
+    v = np.ascontiguousarray(values, np.float32).reshape(-1)
+    return np.array([lib().orc_f32_to_f16(float(x)) for x in v], np.uint16)
+
+
+def f16_value(bits) -> np.ndarray:
+    b = np.asarray(bits, np.uint16).reshape(-1)
+    return np.array([lib().orc_f16_to_f64(int(h)) for h in b], np.float64)
+
+
+def qmatmul_sb4_ref(X: np.ndarray, m: SB4Mat):
+    """Reference for the super-block GEMV/GEMM: exact fp64 weights, fp64 sums."""
+    return matmul_f64(X, m.dequant_f64())
 
 
 # --------------------------------------------------------------------------

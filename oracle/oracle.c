@@ -601,3 +601,166 @@ int32_t orc_rmsnorm_f64(const float* x, const float* g, int64_t T, int64_t H, do
   }
   return 0;
 }
+
+/*
+ * Two-level "super-block" 4-bit format.  "ds4 code walkthrough", trace 4
+ * (quant block struct sizes) prints the block: an fp16 d, an fp16 dmin, 12
+ * bytes of scales and 128 bytes of nibbles for 256 weights, 144 bytes in all.
+ * The pages fix only those fields and sizes; the arithmetic is this reading
+ * of them:
+ *   - a block covers 256 consecutive weights of a row (along K) in 8
+ *     sub-blocks of 32;
+ *   - sub-block j has a 6-bit scale sc_j and a 6-bit min m_j; the 12 bytes
+ *     hold sc_0..sc_7 then m_0..m_7 as consecutive 6-bit fields of one
+ *     little-endian 96-bit integer (field i at bits 6i .. 6i+5);
+ *   - weight 2i is the low nibble of byte i of the 128, weight 2i+1 the high
+ *     nibble (the same byte order as the 4-bit codes of the group format);
+ *   - weight w of sub-block j dequantizes to d*sc_j*q - dmin*m_j.
+ * Quantizer (the pages print none; this follows the group rule of [P1] §3.2
+ * level by level, in fp32 with roundf):
+ *   off_j = max(0, -min_j), step s_j = (max_j + off_j) / 15  (the 16 levels
+ *   -off_j .. 15 s_j - off_j cover the sub-block, 0 included);
+ *   d = fp16(max_j s_j / 63), dmin = fp16(max_j off_j / 63), rounded to
+ *   nearest even;
+ *   sc_j = clamp(round(s_j / d), 0, 63), m_j = clamp(round(off_j / dmin), 0, 63)
+ *   (0 when the divisor is 0);
+ *   q = clamp(round((w + dmin*m_j) / (d*sc_j)), 0, 15) (0 when d*sc_j is 0).
+ * A block holding a NaN or an infinity, or whose d or dmin overflows fp16, is
+ * stored as all zeros and flagged (NONFINITE / DEGENERATE).
+ */
+#define ORC_SB_K 256
+#define ORC_SB_BYTES 144
+
+/* fp32 -> IEEE binary16 bits, round to nearest, ties to even; subnormal
+   results kept, overflow to infinity, NaN to a quiet NaN. */
+uint16_t orc_f32_to_f16(float f) {
+  uint32_t x;
+  memcpy(&x, &f, sizeof x);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7fffffffu;
+  if (ax >= 0x7f800000u) return (uint16_t)(sign | (ax > 0x7f800000u ? 0x7e00u : 0x7c00u));
+  if (ax < 0x00800000u) return (uint16_t)sign; /* fp32 subnormal: far below 2^-25 */
+  const int e = (int)(ax >> 23) - 127;
+  if (e > 15) return (uint16_t)(sign | 0x7c00u);
+  const uint32_t mant = (ax & 0x7fffffu) | 0x800000u; /* 24-bit significand */
+  const int shift = e >= -14 ? 13 : 13 + (-14 - e);   /* bits dropped */
+  if (shift > 24) return (uint16_t)sign;
+  uint32_t q = mant >> shift;
+  const uint32_t rem = mant & ((1u << shift) - 1u), half = 1u << (shift - 1);
+  if (rem > half || (rem == half && (q & 1u))) ++q;
+  /* normal: q holds the implicit bit (0x400 .. 0x800, a carry moves the
+     exponent up); subnormal: q is the fraction itself */
+  const uint32_t h = e >= -14 ? ((uint32_t)(e + 14) << 10) + q : q;
+  return (uint16_t)(sign | (h >= 0x7c00u ? 0x7c00u : h));
+}
+
+/* binary16 bits -> its exact value */
+double orc_f16_to_f64(uint16_t h) {
+  const int e = (h >> 10) & 31, m = h & 0x3ff;
+  double v;
+  if (e == 0) v = ldexp((double)m, -24);
+  else if (e == 31) v = m ? NAN : INFINITY;
+  else v = ldexp((double)(m + 1024), e - 25);
+  return (h & 0x8000u) ? -v : v;
+}
+
+static uint32_t orc_sb_field(const uint8_t* s12, int i) {
+  uint32_t v = 0;
+  for (int b = 0; b < 6; ++b) {
+    const int bit = 6 * i + b;
+    v |= (uint32_t)((s12[bit >> 3] >> (bit & 7)) & 1u) << b;
+  }
+  return v;
+}
+
+static void orc_sb_set_field(uint8_t* s12, int i, uint32_t v) {
+  for (int b = 0; b < 6; ++b) {
+    const int bit = 6 * i + b;
+    if ((v >> b) & 1u) s12[bit >> 3] |= (uint8_t)(1u << (bit & 7));
+  }
+}
+
+/* Quantizes w[rows][K] (K % 256 == 0) into blocks[rows][K/256][144]; flags
+   gets one byte per block.  Returns the number of flagged blocks, -1 for
+   invalid arguments. */
+int64_t orc_sb4_quantize(const float* w, int64_t rows, int64_t K, uint8_t* blocks,
+                         uint8_t* bflags) {
+  if (!w || !blocks || rows < 0 || K <= 0 || K % ORC_SB_K != 0) return -1;
+  const int64_t nb = K / ORC_SB_K;
+  int64_t nflag = 0;
+#pragma omp parallel for schedule(static) reduction(+ : nflag)
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t b = 0; b < nb; ++b) {
+      const float* src = w + r * K + b * ORC_SB_K;
+      uint8_t* out = blocks + (r * nb + b) * ORC_SB_BYTES;
+      memset(out, 0, ORC_SB_BYTES);
+      uint8_t flag = 0;
+      float step[8], off[8];
+      float smax = 0.0f, omax = 0.0f;
+      for (int j = 0; j < 8; ++j) {
+        float lo = FLT_MAX, hi = -FLT_MAX;
+        for (int i = 0; i < 32; ++i) {
+          const float v = src[32 * j + i];
+          if (!isfinite(v)) flag |= ORC_FLAG_NONFINITE;
+          if (v < lo) lo = v;
+          if (v > hi) hi = v;
+        }
+        off[j] = lo < 0.0f ? -lo : 0.0f;
+        step[j] = (hi + off[j]) / 15.0f;
+        if (step[j] > smax) smax = step[j];
+        if (off[j] > omax) omax = off[j];
+      }
+      uint16_t d16 = 0, m16 = 0;
+      if (!flag) {
+        d16 = orc_f32_to_f16(smax / 63.0f);
+        m16 = orc_f32_to_f16(omax / 63.0f);
+        if ((d16 & 0x7c00u) == 0x7c00u || (m16 & 0x7c00u) == 0x7c00u) flag |= ORC_FLAG_DEGENERATE;
+      }
+      if (bflags) bflags[r * nb + b] = flag;
+      if (flag) {
+        ++nflag;
+        continue; /* the block stays all zeros */
+      }
+      const float df = (float)orc_f16_to_f64(d16), mf = (float)orc_f16_to_f64(m16);
+      out[0] = (uint8_t)(d16 & 0xff);
+      out[1] = (uint8_t)(d16 >> 8);
+      out[2] = (uint8_t)(m16 & 0xff);
+      out[3] = (uint8_t)(m16 >> 8);
+      for (int j = 0; j < 8; ++j) {
+        float sc = df > 0.0f ? roundf(step[j] / df) : 0.0f;
+        float mn = mf > 0.0f ? roundf(off[j] / mf) : 0.0f;
+        sc = sc < 0.0f ? 0.0f : (sc > 63.0f ? 63.0f : sc);
+        mn = mn < 0.0f ? 0.0f : (mn > 63.0f ? 63.0f : mn);
+        orc_sb_set_field(out + 4, j, (uint32_t)sc);
+        orc_sb_set_field(out + 4, 8 + j, (uint32_t)mn);
+        const float S = df * sc, M = mf * mn;
+        for (int i = 0; i < 32; ++i) {
+          const int k = 32 * j + i;
+          float q = S > 0.0f ? roundf((src[k] + M) / S) : 0.0f;
+          q = q < 0.0f ? 0.0f : (q > 15.0f ? 15.0f : q);
+          out[16 + k / 2] |= (uint8_t)((uint32_t)q << ((k & 1) * 4));
+        }
+      }
+    }
+  }
+  return nflag;
+}
+
+/* Dequantizes blocks[rows][K/256][144] into out[rows][K] (double, exact). */
+int32_t orc_sb4_dequant_f64(const uint8_t* blocks, int64_t rows, int64_t K, double* out) {
+  if (!blocks || !out || rows < 0 || K <= 0 || K % ORC_SB_K != 0) return -1;
+  const int64_t nb = K / ORC_SB_K;
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < nb; ++b) {
+      const uint8_t* blk = blocks + (r * nb + b) * ORC_SB_BYTES;
+      const double d = orc_f16_to_f64((uint16_t)(blk[0] | (blk[1] << 8)));
+      const double dmin = orc_f16_to_f64((uint16_t)(blk[2] | (blk[3] << 8)));
+      for (int k = 0; k < ORC_SB_K; ++k) {
+        const int j = k / 32;
+        const double q = (double)((blk[16 + k / 2] >> ((k & 1) * 4)) & 15u);
+        out[r * K + b * ORC_SB_K + k] =
+            d * (double)orc_sb_field(blk + 4, j) * q - dmin * (double)orc_sb_field(blk + 4, 8 + j);
+      }
+    }
+  return 0;
+}
