@@ -36,8 +36,9 @@ def log(*a):
 
 
 def qbytes(bits, group, K, N):
-    """Canonical bytes of a quantized matrix: codes + fp32 (scale, zp)."""
-    return N * K * bits // 8 + N * (K // group) * 8
+    """Canonical bytes of a quantized matrix: codes + fp32 (scale, zp), or for
+    the super-block format (group 256) codes + a 16-byte header per block."""
+    return N * K * bits // 8 + N * (K // group) * (16 if group == 256 else 8)
 
 
 # the sources that define the dominant kernel (the fused-dequant GEMV)
@@ -101,7 +102,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cases", default="head,gemv8,gemv4,moe1,block1,moe32,gemm256,moe256",
+    ap.add_argument("--cases", default="head,gemv8,gemv4,sb4,sb4vocab,moe1,block1,moe32,gemm256,"
+                                       "moe256",
                     help="secondary workloads to run (comma list)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -255,7 +257,27 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
         rotated_gemv(8, 64, "INT8 g64 GEMV 4096x4096 (M=1)", 64)
     if "gemv4" in cases:
         rotated_gemv(4, 64, "INT4 g64 GEMV 4096x4096 (M=1)", 64)
+    if "sb4" in cases:
+        rotated_gemv(4, 256, "super-block 4-bit GEMV 4096x4096 (M=1)", 64)
     torch.cuda.empty_cache()
+    if "sb4vocab" in cases:
+        # the vocab projection in the super-block format: 298 MB, cold by size
+        NV = 129280
+        w = synth.normal((NV, K), 0.02, 0, synth.W, 2, device=dev)
+        q = dsq.QWeight(4, 256, K, NV)
+        dsq.pack_weights(w, q)
+        del w
+        torch.cuda.empty_cache()
+        y = torch.empty(NV, device=dev)
+        ms = time_calls(lambda i: dsq.gemv(q, x, y), 100, 1, torch)
+        b = qbytes(4, 256, K, NV) + K * 4 + NV * 4
+        gbs = b / (ms * 1e-3) / 1e9
+        out.append({"workload": "super-block 4-bit vocab GEMV 4096x129280 (M=1)",
+                    "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": b})
+        log(out[-1])
+        del q
+        torch.cuda.empty_cache()
 
     # MoE decode layers: 256 experts, H=4096, I=2048, top-6
     def build_moe(bits, group, bias_std):

@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsq.so")
-SOURCES = ["api.hip", "pack.hip", "gemv.hip", "decode.hip", "route.hip",
+SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemv_sb4.hip", "decode.hip", "route.hip",
            "gemm_mfma.hip",
            "gmm.hip", "head.hip"]
 

@@ -28,7 +28,8 @@ bool mul_ok(int64_t a, int64_t b, int64_t lim = int64_t(1) << 62) {
 // Shape rules of a packed weight (without the pointer).
 dsq_status check_shape(int32_t bits, int32_t group, int64_t K, int64_t N, int64_t batch) {
   if (bits != 8 && bits != 4) return DSQ_ERR_INVALID_ARG;
-  if (group != 64 && group != 128) return DSQ_ERR_INVALID_ARG;
+  if (group != 64 && group != 128 && !(group == kSuperGroup && bits == 4))
+    return DSQ_ERR_INVALID_ARG;
   if (K <= 0 || N <= 0 || batch <= 0) return DSQ_ERR_SHAPE;
   if (K % group != 0) return DSQ_ERR_SHAPE;
   if (K > kMaxDim || N > kMaxDim || batch > kMaxDim) return DSQ_ERR_OVERFLOW;
@@ -223,6 +224,7 @@ dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float*
   if (M > kMaxDim || !mul_ok(M, W->K) || !mul_ok(M, W->N)) return DSQ_ERR_OVERFLOW;
   if (!aligned(X, 16) || !aligned(Y, 4)) return DSQ_ERR_ALIGN;
   const bool bf16 = use_bf16(math, M);
+  if (W->group == kSuperGroup && (M >= 2 || bf16)) return DSQ_ERR_UNSUPPORTED;  // GEMV only
   if (M >= 2 || bf16) {
     const size_t need = dsq_gemm_workspace_bytes(M, W->N, W->K, math);
     if (need == 0) return DSQ_ERR_UNSUPPORTED;
@@ -331,6 +333,7 @@ dsq_status check_moe(const float* X, const float* router_w, const float* bias,
   if (up->bits != gate->bits || down->bits != gate->bits || up->group != gate->group ||
       down->group != gate->group)
     return DSQ_ERR_SHAPE;
+  if (gate->group == kSuperGroup) return DSQ_ERR_UNSUPPORTED;  // GEMV only
   if (T < 0 || top_k <= 0 || top_k > E64) return DSQ_ERR_SHAPE;
   if (T > 65536 || E64 > 4096 || top_k > 32) return DSQ_ERR_UNSUPPORTED;
   if (!aligned(X, 16) || !aligned(router_w, 16) || !aligned(Y, 16) || (bias && !aligned(bias, 4)))

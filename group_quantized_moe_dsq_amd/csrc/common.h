@@ -12,11 +12,20 @@ constexpr int kWave = 64;
 
 __host__ __device__ inline int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
 
+// group = 256 (4-bit only) selects the two-level super-block format: the
+// metadata of a group is then a 16-byte block header (fp16 d, fp16 dmin,
+// twelve bytes of 6-bit sub-block scales and mins) instead of the
+// (float scale, float zero point) pair.
+constexpr int kSuperGroup = 256;
+__host__ __device__ inline int meta_bytes_per_group(int group) {
+  return group == kSuperGroup ? 16 : 8;
+}
+
 // Byte geometry of one packed batch entry (layout version 1, see dsq.h).
 struct Layout {
   int64_t row_bytes;     // K * bits / 8
   int64_t groups;        // K / group
-  int64_t meta_off;      // offset of the (scale, zp) table inside an entry
+  int64_t meta_off;      // offset of the metadata table inside an entry
   int64_t stride;        // bytes per batch entry
 };
 
@@ -25,7 +34,7 @@ __host__ __device__ inline Layout layout_of(int bits, int group, int64_t K, int6
   L.row_bytes = K * bits / 8;
   L.groups = K / group;
   L.meta_off = align256(N * L.row_bytes);
-  L.stride = L.meta_off + align256(N * L.groups * 8);
+  L.stride = L.meta_off + align256(N * L.groups * meta_bytes_per_group(group));
   return L;
 }
 

@@ -195,6 +195,7 @@ hipError_t dispatch(const QMat& q, const float* x, float* y, int N, int K, int g
 
 hipError_t launch_gemv(const dsq_qweight& W, int64_t expert, const float* x, float* y,
                        hipStream_t stream) {
+  if (W.group == kSuperGroup) return launch_gemv_sb4(W, expert, x, y, stream);
   const QMat q = entry(W, expert);
   const int N = int(W.N), K = int(W.K);
   if (W.bits == 8) return dispatch<8>(q, x, y, N, K, W.group, stream);

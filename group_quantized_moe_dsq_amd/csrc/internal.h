@@ -11,9 +11,12 @@ namespace dsq {
 hipError_t launch_pack(const float* src, const dsq_qweight& W, int64_t first, int64_t count,
                        int32_t* flags, hipStream_t stream);
 
-// y = W[expert] x  (M = 1)
+// y = W[expert] x  (M = 1); the super-block format (group 256) goes to
+// launch_gemv_sb4 (gemv_sb4.hip)
 hipError_t launch_gemv(const dsq_qweight& W, int64_t expert, const float* x, float* y,
                        hipStream_t stream);
+hipError_t launch_gemv_sb4(const dsq_qweight& W, int64_t expert, const float* x, float* y,
+                           hipStream_t stream);
 
 // Routing description for the grouped kernels.  In dense mode `active` is
 // NULL and the single "expert" covers tokens 0..M-1.

@@ -84,12 +84,32 @@ typedef int32_t dsq_status;
  *               integer held in fp32.
  *   stride = align256(N * RB) + align256(N * (K/group) * 8).
  * A flagged group has all its codes 0 and scale = zero point = 0.
+ *
+ * group = 256 (bits = 4 only) selects the two-level super-block format, the
+ * block of "ds4 code walkthrough", trace 4 (quant block struct sizes): fp16 d,
+ * fp16 dmin, 12 bytes of scales, 128 bytes of nibbles per 256 weights.  Its
+ * arithmetic is read from those fields: 8 sub-blocks of 32 weights; sub-block
+ * j has a 6-bit scale sc_j and a 6-bit min m_j; a weight dequantizes to
+ * d*sc_j*q - dmin*m_j.  Quantizer, in fp32 with roundf:
+ *   off_j = max(0, -min_j), step_j = (max_j + off_j) / 15,
+ *   d = fp16(max step / 63), dmin = fp16(max off / 63) (nearest even),
+ *   sc_j = clamp(round(step_j / d), 0, 63), m_j = clamp(round(off_j / dmin), 0, 63),
+ *   q = clamp(round((w + dmin*m_j) / (d*sc_j)), 0, 15)  (0 when a divisor is 0).
+ * Layout: the payload as the 4-bit group format (a 16-byte chunk is one
+ * sub-block); the metadata holds per row K/256 16-byte block headers:
+ * word 0 = d | dmin << 16 (fp16 bits), words 1..3 = a little-endian 96-bit
+ * field stream with sc_0..sc_7 then m_0..m_7, field f at bits 6f..6f+5.
+ *   stride = align256(N * K/2) + align256(N * (K/256) * 16)
+ * A block holding a NaN or infinity (DSQ_FLAG_NONFINITE), or whose d or dmin
+ * overflows fp16 (DSQ_FLAG_DEGENERATE), is stored as zeros.  This format is
+ * read by dsq_gemv and dsq_gemv_topk; dsq_gemm with M >= 2, dsq_moe_ffn and
+ * dsq_moe_block return DSQ_ERR_UNSUPPORTED for it.
  */
 #define DSQ_LAYOUT_VERSION 1u
 
 typedef struct dsq_qweight {
   int32_t bits;            /* 8 or 4                                          */
-  int32_t group;           /* 64 or 128, along K                              */
+  int32_t group;           /* 64 or 128 along K; 256 = super-block (4-bit)    */
   int64_t K;               /* reduction length (columns of W)                 */
   int64_t N;               /* outputs (rows of W)                             */
   int64_t batch;           /* number of matrices (experts); 1 for dense       */

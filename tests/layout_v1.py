@@ -17,12 +17,33 @@ def geometry(bits, group, K, N):
     rb = K * bits // 8
     ng = K // group
     meta_off = align256(N * rb)
-    stride = meta_off + align256(N * ng * 8)
+    stride = meta_off + align256(N * ng * (16 if group == 256 else 8))
     return rb, ng, meta_off, stride
 
 
 def packed_bytes(bits, group, K, N, batch):
     return geometry(bits, group, K, N)[3] * batch
+
+
+def nibbles_to_canonical(payload: np.ndarray, N: int, K: int) -> np.ndarray:
+    """4-bit device words -> canonical bytes (k = 2j low nibble, 2j+1 high)."""
+    # device word j: byte i holds k = 8j+i (low nibble) and k = 8j+4+i (high)
+    words = payload.reshape(N, K // 8, 4)
+    codes = np.empty((N, K // 8, 8), np.uint8)
+    codes[:, :, 0:4] = words & 0x0F
+    codes[:, :, 4:8] = words >> 4
+    codes = codes.reshape(N, K)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def decode_sb_entry(buf: np.ndarray, b: int, K: int, N: int) -> np.ndarray:
+    """Super-block format (group 256): the canonical 144-byte blocks
+    [N][K/256][144] = 16-byte header, then the 128 canonical code bytes."""
+    rb, nb, meta_off, stride = geometry(4, 256, K, N)
+    base = b * stride
+    canon = nibbles_to_canonical(buf[base:base + N * rb], N, K).reshape(N, nb, 128)
+    hdr = buf[base + meta_off:base + meta_off + N * nb * 16].reshape(N, nb, 16)
+    return np.concatenate([hdr, canon], axis=-1)
 
 
 def decode_entry(buf: np.ndarray, b: int, bits: int, group: int, K: int, N: int):
@@ -35,14 +56,7 @@ def decode_entry(buf: np.ndarray, b: int, bits: int, group: int, K: int, N: int)
     zp = np.ascontiguousarray(meta[:, :, 1])
     if bits == 8:
         return np.ascontiguousarray(payload), scale, zp
-    # device word j: byte i holds k = 8j+i (low nibble) and k = 8j+4+i (high)
-    words = payload.reshape(N, K // 8, 4)
-    codes = np.empty((N, K // 8, 8), np.uint8)
-    codes[:, :, 0:4] = words & 0x0F
-    codes[:, :, 4:8] = words >> 4
-    codes = codes.reshape(N, K)
-    canon = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
-    return canon, scale, zp
+    return nibbles_to_canonical(payload, N, K), scale, zp
 
 
 def encode_entry(q_canon: np.ndarray, scale, zp, bits, group, K, N) -> np.ndarray:

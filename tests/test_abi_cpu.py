@@ -131,6 +131,25 @@ def test_moe_validation_and_workspace_query():
     assert dsq.moe_workspace_bytes(5, E, 9, H, I, 0) == 0
 
 
+def test_superblock_format_shapes_and_limits():
+    # group 256 is the 4-bit super-block format: 16-byte block headers
+    N, K = 10, 512
+    assert dsq.packed_bytes(4, 256, K, N) == layout_v1.packed_bytes(4, 256, K, N, 1)
+    assert dsq.packed_bytes(4, 256, K, N) == 2560 + 512   # align256(N*K/2) + align256(N*2*16)
+    assert dsq.packed_bytes(8, 256, K, N) == 0            # 8-bit super-blocks: no
+    assert dsq.packed_bytes(4, 256, 384, N) == 0          # K % 256 != 0
+    L = dsq.lib()
+    g, rg = desc(4, 256, 256, 256, 4)
+    u, ru = desc(4, 256, 256, 256, 4)
+    dn, rd = desc(4, 256, 256, 256, 4)
+    assert rg == ru == rd == 0
+    fake = ctypes.c_void_p(0x40000)
+    # the matrix-core paths do not read it
+    assert L.dsq_moe_ffn(fake, fake, None, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), 5,
+                         2, 0, fake, fake, 1 << 30, None, None, None, None, None) == -5
+    assert L.dsq_gemm(ctypes.byref(g), 0, fake, fake, 8, 0, fake, 1 << 30, None) == -5
+
+
 def test_moe_block_validation_and_workspace_query():
     L = dsq.lib()
     H, I, E = 256, 128, 8
