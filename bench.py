@@ -102,8 +102,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cases", default="head,gemv8,gemv4,sb4,sb4vocab,moe1,block1,moe32,gemm256,"
-                                       "moe256",
+    ap.add_argument("--cases", default="head,gemv8,gemv4,sb4,sb4vocab,moe1,block1,cache,moe32,"
+                                       "gemm256,moe256",
                     help="secondary workloads to run (comma list)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -326,7 +326,7 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
         out.append(rec)
         log(rec)
 
-    if "moe1" in cases or "moe32" in cases or "block1" in cases:
+    if "moe1" in cases or "moe32" in cases or "block1" in cases or "cache" in cases:
         r, b, g, u, d = build_moe(4, 64, None)
         if "moe1" in cases:
             moe_case("MoE decode T=1, 256 experts top-6, INT4 g64 SwiGLU",
@@ -335,6 +335,8 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
             moe_case("MoE block decode T=1 (RMSNorm + MoE + residual), INT4 g64 SwiGLU",
                      dsq.MoeLayer(r, g, u, d, None, 6), 1, 64, dsq.MATH_FP32, 4, 64, 64,
                      block=True)
+        if "cache" in cases:
+            expert_cache_case(dsq, synth, torch, dev, r, (g, u, d), out)
         if "moe32" in cases:
             bias = synth.normal((256,), 1.0, 0, synth.BIAS, 0, device=dev)
             moe_case("MoE batched decode T=32 skewed (router bias ~N(0,1)), INT4 g64",
@@ -350,6 +352,45 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
         del g, u, d
         torch.cuda.empty_cache()
     return out
+
+
+def expert_cache_case(dsq, synth, torch, dev, router, layer, out):
+    """Decode tokens through the full MoE layer with its 256 experts in
+    pinned host memory and an HBM cache of `slots` experts (least recently
+    used out): time per token, hit rate, host-to-device copy rate.  The
+    routing of random activations is spread over all experts, so the hit
+    rate follows the cache's share of them."""
+    import time
+    H, I, E, k = 4096, 2048, 256, 6
+    for slots in (16, 64, 256):
+        c = dsq.ExpertCache(4, 64, H, I, E, slots, device=dev)
+        for m, q in enumerate(layer):
+            c.host[m].copy_(q.buf)
+        ws = torch.empty(dsq.moe_cached_workspace_bytes(1, E, slots, k, H, I, dsq.MATH_FP32) + 256,
+                         dtype=torch.uint8, device=dev)
+        Y = torch.empty((1, H), device=dev)
+        Xs = [synth.normal((1, H), 1.0, 0, synth.X, 5000 + t, device=dev) for t in range(96)]
+        torch.cuda.synchronize()
+        for t in range(32):                    # fill the cache
+            dsq.moe_ffn_cached(router, None, c, Xs[t], k, math=dsq.MATH_FP32, Y=Y, workspace=ws)
+        h0, m0, b0 = c.hits, c.misses, c.bytes_copied
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for t in range(32, 96):
+            dsq.moe_ffn_cached(router, None, c, Xs[t], k, math=dsq.MATH_FP32, Y=Y, workspace=ws)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 64
+        hits, misses, nbytes = c.hits - h0, c.misses - m0, c.bytes_copied - b0
+        rec = {"workload": f"MoE decode T=1 with the experts behind an HBM cache of {slots} of 256 "
+                           "(pinned host store, LRU), INT4 g64",
+               "us_per_token": round(dt * 1e6, 1),
+               "hit_rate": round(hits / max(hits + misses, 1), 3),
+               "h2d_GB_per_token": round(nbytes / 64 / 1e9, 4),
+               "h2d_GB/s": round(nbytes / (dt * 64) / 1e9, 1)}
+        out.append(rec)
+        log(rec)
+        del c, ws
+        torch.cuda.empty_cache()
 
 
 def dense_prefill(dsq, synth, torch, dev):

@@ -4,7 +4,8 @@
 // up-front shape validation of "ds4 code walkthrough", Part 1, trace 5),
 // returns a status instead of exiting, allocates nothing (callers pass
 // workspace; the same walkthrough forbids allocation in the token loop) and
-// only enqueues kernels on the caller's stream.
+// only enqueues work on the caller's stream (dsq_moe_ffn_cached alone waits
+// for it once: the host must see the routing to fetch experts).
 #include <float.h>
 #include <string.h>
 
@@ -347,11 +348,14 @@ dsq_status check_moe(const float* X, const float* router_w, const float* bias,
 // The MoE layer of the pages (§3.5) on the rows X.  With gamma the rows are
 // RMS-normalised into xn first and the experts see xn (§2.1: RMSNorm before
 // the MoE step); with resid the residual is added to Y.
+// With given_idx/given_w the routing is given (entries index the weight
+// batches, e.g. expert-cache slots): no router and no top-k run.
 dsq_status run_moe(const float* X, const float* gamma, float eps, float* xn, const float* resid,
                    const float* router_w, const float* bias, const dsq_qweight& gate,
                    const dsq_qweight& up, const dsq_qweight& down, int64_t T, int32_t top_k,
                    bool bf16, float* Y, void* workspace, float* logits_out, int32_t* idx_out,
-                   float* w_out, int32_t* expert_counts_out, hipStream_t st) {
+                   float* w_out, int32_t* expert_counts_out, const int32_t* given_idx,
+                   const float* given_w, hipStream_t st) {
   const int32_t E = int32_t(gate.batch);
   const int64_t E64 = gate.batch, H = gate.K, I = gate.N;
   MoeWs m{};
@@ -360,6 +364,11 @@ dsq_status run_moe(const float* X, const float* gamma, float eps, float* xn, con
   if (idx_out) m.idx = idx_out;
   if (w_out) m.w = w_out;
   if (expert_counts_out) m.counts = expert_counts_out;
+  const bool given = given_idx != nullptr;
+  if (given) {
+    m.idx = const_cast<int32_t*>(given_idx);  // only read
+    m.w = const_cast<float*>(given_w);
+  }
   // the rows the experts (and a separate router) read
   const float* Xe = gamma ? xn : X;
   hipError_t e;
@@ -368,24 +377,27 @@ dsq_status run_moe(const float* X, const float* gamma, float eps, float* xn, con
   if (!bf16 && T <= kDecodeMaxTokens && decode_supported(gate.bits, H, I, E, top_k)) {
     // Decode: every (token, slot) pair is its own GEMV; no grouping needed.
     // The gate/up kernel ranks the scores itself and publishes idx/w.
-    DSQ_TRY(launch_router_gemv(X, T, router_w, bias, E, H, m.logits, gamma, eps, xn, st));
-    DSQ_TRY(launch_moe_decode(gate, up, down, Xe, T, E, top_k, m.logits, m.idx, m.w,
-                              static_cast<float*>(m.hbuf), Y, resid, st));
+    if (!given)
+      DSQ_TRY(launch_router_gemv(X, T, router_w, bias, E, H, m.logits, gamma, eps, xn, st));
+    DSQ_TRY(launch_moe_decode(gate, up, down, Xe, T, E, top_k, given ? nullptr : m.logits, m.idx,
+                              m.w, static_cast<float*>(m.hbuf), Y, resid, st));
     if (expert_counts_out) {
       DSQ_TRY(launch_group(m.idx, T, top_k, E, m.bitmap, m.counts, m.offsets, m.perm, m.pos,
                            m.active, m.n_active, st));
     }
     return DSQ_OK;
   }
-  // (0) + (1) normalisation and router logits, fp32, bias included
-  if (T <= 32) {
-    DSQ_TRY(launch_router_gemv(X, T, router_w, bias, E, H, m.logits, gamma, eps, xn, st));
-  } else {
-    if (gamma) DSQ_TRY(launch_rmsnorm(X, gamma, T, H, eps, xn, st));
-    DSQ_TRY(launch_router(Xe, T, router_w, bias, E, H, m.logits, st));
+  if (!given) {
+    // (0) + (1) normalisation and router logits, fp32, bias included
+    if (T <= 32) {
+      DSQ_TRY(launch_router_gemv(X, T, router_w, bias, E, H, m.logits, gamma, eps, xn, st));
+    } else {
+      if (gamma) DSQ_TRY(launch_rmsnorm(X, gamma, T, H, eps, xn, st));
+      DSQ_TRY(launch_router(Xe, T, router_w, bias, E, H, m.logits, st));
+    }
+    // (2) softmax + top-k + renormalisation
+    DSQ_TRY(launch_topk(m.logits, nullptr, T, E, top_k, m.idx, m.w, st));
   }
-  // (2) softmax + top-k + renormalisation
-  DSQ_TRY(launch_topk(m.logits, nullptr, T, E, top_k, m.idx, m.w, st));
   // (3) stable grouping by expert
   DSQ_TRY(launch_group(m.idx, T, top_k, E, m.bitmap, m.counts, m.offsets, m.perm, m.pos, m.active,
                        m.n_active, st));
@@ -430,7 +442,7 @@ dsq_status dsq_moe_ffn(const float* X, const float* router_w, const float* bias,
   if ((s = check_device()) != DSQ_OK) return s;
   return run_moe(X, nullptr, 0.0f, nullptr, nullptr, router_w, bias, *gate, *up, *down, T, top_k,
                  use_bf16(math, T), Y, workspace, logits_out, idx_out, w_out, expert_counts_out,
-                 (hipStream_t)stream);
+                 nullptr, nullptr, (hipStream_t)stream);
 }
 
 size_t dsq_moe_block_workspace_bytes(int64_t T, int32_t E, int32_t top_k, int64_t H, int64_t I,
@@ -464,7 +476,208 @@ dsq_status dsq_moe_block(const float* X, const float* norm_w, float eps, const f
   float* xn = xn_out ? xn_out : reinterpret_cast<float*>(ws);
   return run_moe(X, norm_w, eps, xn, X, router_w, bias, *gate, *up, *down, T, top_k,
                  use_bf16(math, T), Y, ws + align256(T * gate->K * 4), logits_out, idx_out, w_out,
-                 expert_counts_out, (hipStream_t)stream);
+                 expert_counts_out, nullptr, nullptr, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// Expert cache ("Running a 284B-parameter LLM from 3.2 GB of RAM in plain C":
+// the router picks the experts, only those are streamed into an LRU cache).
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+
+int64_t entry_stride(const dsq_qweight& W) { return layout_of(W.bits, W.group, W.K, W.N).stride; }
+
+dsq_status check_cache(const dsq_expert_cache* c) {
+  if (!c || !c->host_gate || !c->host_up || !c->host_down || !c->slot_of || !c->expert_of ||
+      !c->last_use || c->E < 1)
+    return DSQ_ERR_INVALID_ARG;
+  dsq_status s;
+  if ((s = check_qweight(&c->gate)) != DSQ_OK) return s;
+  if ((s = check_qweight(&c->up)) != DSQ_OK) return s;
+  if ((s = check_qweight(&c->down)) != DSQ_OK) return s;
+  const int64_t H = c->gate.K, I = c->gate.N, S = c->gate.batch;
+  if (c->up.batch != S || c->down.batch != S || c->slots != S) return DSQ_ERR_SHAPE;
+  if (c->up.K != H || c->up.N != I || c->down.K != I || c->down.N != H) return DSQ_ERR_SHAPE;
+  if (c->up.bits != c->gate.bits || c->down.bits != c->gate.bits ||
+      c->up.group != c->gate.group || c->down.group != c->gate.group)
+    return DSQ_ERR_SHAPE;
+  if (c->gate.group == kSuperGroup) return DSQ_ERR_UNSUPPORTED;
+  return DSQ_OK;
+}
+
+// Maps experts[0..n) to slots as one call; fill(expert, slot) for each miss.
+template <class Fill>
+dsq_status cache_map(dsq_expert_cache* c, const int32_t* experts, int64_t n, int32_t* slot_out,
+                     Fill&& fill) {
+  const uint64_t now = ++c->clock;
+  for (int64_t i = 0; i < n; ++i) {
+    const int32_t e = experts[i];
+    if (e < 0 || e >= c->E) return DSQ_ERR_INVALID_ARG;
+    int32_t s = c->slot_of[e];
+    if (s >= 0) {
+      ++c->hits;
+    } else {
+      // an empty slot (stamp 0) first, else the least recently used slot
+      // that this call has not used; ties go to the lowest index
+      int32_t v = -1;
+      uint64_t best = ~uint64_t(0);
+      for (int32_t j = 0; j < c->slots; ++j) {
+        const uint64_t t = c->expert_of[j] < 0 ? 0 : c->last_use[j];
+        if (t < now && t < best) {
+          best = t;
+          v = j;
+        }
+      }
+      if (v < 0) return DSQ_ERR_UNSUPPORTED;
+      if (c->expert_of[v] >= 0) c->slot_of[c->expert_of[v]] = -1;
+      c->expert_of[v] = e;
+      c->slot_of[e] = v;
+      s = v;
+      ++c->misses;
+      const dsq_status f = fill(e, v);
+      if (f != DSQ_OK) return f;
+    }
+    c->last_use[s] = now;
+    if (slot_out) slot_out[i] = s;
+  }
+  return DSQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsq_status dsq_expert_cache_init(dsq_expert_cache* cache, const dsq_qweight* gate,
+                                 const dsq_qweight* up, const dsq_qweight* down,
+                                 const void* host_gate, const void* host_up,
+                                 const void* host_down, int32_t E, int32_t* slot_of,
+                                 int32_t* expert_of, uint64_t* last_use) {
+  if (!cache || !gate || !up || !down) return DSQ_ERR_INVALID_ARG;
+  dsq_expert_cache c{};
+  c.gate = *gate;
+  c.up = *up;
+  c.down = *down;
+  c.host_gate = host_gate;
+  c.host_up = host_up;
+  c.host_down = host_down;
+  c.E = E;
+  c.slots = gate->batch > INT32_MAX ? -1 : int32_t(gate->batch);
+  c.slot_of = slot_of;
+  c.expert_of = expert_of;
+  c.last_use = last_use;
+  const dsq_status s = check_cache(&c);
+  if (s != DSQ_OK) return s;
+  for (int32_t e = 0; e < E; ++e) slot_of[e] = -1;
+  for (int32_t j = 0; j < c.slots; ++j) {
+    expert_of[j] = -1;
+    last_use[j] = 0;
+  }
+  *cache = c;
+  return DSQ_OK;
+}
+
+dsq_status dsq_expert_cache_plan(dsq_expert_cache* cache, const int32_t* experts, int64_t n,
+                                 int32_t* slot_out, int32_t* fill_expert, int32_t* fill_slot,
+                                 int64_t* n_fill) {
+  dsq_status s = check_cache(cache);
+  if (s != DSQ_OK) return s;
+  if (n < 0 || (n > 0 && (!experts || !slot_out || !fill_expert || !fill_slot)) || !n_fill)
+    return DSQ_ERR_INVALID_ARG;
+  int64_t nf = 0;
+  s = cache_map(cache, experts, n, slot_out, [&](int32_t e, int32_t v) {
+    fill_expert[nf] = e;
+    fill_slot[nf] = v;
+    ++nf;
+    return DSQ_OK;
+  });
+  *n_fill = nf;
+  return s;
+}
+
+size_t dsq_moe_cached_workspace_bytes(int64_t T, int32_t E, int32_t slots, int32_t top_k,
+                                      int64_t H, int64_t I, int32_t math) {
+  if (E < 1 || E > 4096) return 0;
+  const size_t moe = dsq_moe_workspace_bytes(T, slots, top_k, H, I, math);
+  if (moe == 0) return 0;
+  // router logits [T][E], expert ids, weights and slots [T][k]
+  return size_t(align256(T * E * 4) + 3 * align256(T * top_k * 4)) + moe;
+}
+
+dsq_status dsq_moe_ffn_cached(const float* X, const float* router_w, const float* bias,
+                              dsq_expert_cache* cache, int64_t T, int32_t top_k, int32_t math,
+                              float* Y, void* workspace, size_t workspace_bytes,
+                              int32_t* host_idx, int32_t* host_slots, float* logits_out,
+                              int32_t* idx_out, float* w_out, void* stream) {
+  dsq_status s = check_cache(cache);
+  if (s != DSQ_OK) return s;
+  if ((s = check_moe(X, router_w, bias, &cache->gate, &cache->up, &cache->down, T, top_k, math, Y,
+                     logits_out, idx_out, w_out, nullptr)) != DSQ_OK)
+    return s;
+  if (top_k > cache->E) return DSQ_ERR_SHAPE;
+  if (T > 0 && (!host_idx || !host_slots)) return DSQ_ERR_INVALID_ARG;
+  const int32_t E = cache->E;
+  const int64_t H = cache->gate.K, I = cache->gate.N;
+  const size_t need = dsq_moe_cached_workspace_bytes(T, E, cache->slots, top_k, H, I, math);
+  if (need == 0) return DSQ_ERR_OVERFLOW;
+  if (!workspace || workspace_bytes < need) return DSQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return DSQ_ERR_ALIGN;
+  if (T == 0) return DSQ_OK;
+  if ((s = check_device()) != DSQ_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  Carver cv(workspace);
+  float* logits = static_cast<float*>(cv.take(T * E, 4));
+  int32_t* idx = static_cast<int32_t*>(cv.take(T * top_k, 4));
+  float* w = static_cast<float*>(cv.take(T * top_k, 4));
+  int32_t* slots_dev = static_cast<int32_t*>(cv.take(T * top_k, 4));
+  void* moe_ws = static_cast<uint8_t*>(workspace) + cv.used;
+  if (logits_out) logits = logits_out;
+  if (idx_out) idx = idx_out;
+  if (w_out) w = w_out;
+  hipError_t e;
+#define DSQ_TRY(call)                          \
+  if ((e = (call)) != hipSuccess) return hip_status(e);
+  // (1) routing on the GPU
+  if (T <= 32) {
+    DSQ_TRY(launch_router_gemv(X, T, router_w, bias, E, H, logits, nullptr, 0.0f, nullptr, st));
+  } else {
+    DSQ_TRY(launch_router(X, T, router_w, bias, E, H, logits, st));
+  }
+  DSQ_TRY(launch_topk(logits, nullptr, T, E, top_k, idx, w, st));
+  // (2) the host sees the routing
+  const size_t nb = size_t(T * top_k) * 4;
+  DSQ_TRY(hipMemcpyAsync(host_idx, idx, nb, hipMemcpyDeviceToHost, st));
+  DSQ_TRY(hipStreamSynchronize(st));
+  // (3) slots for the requested experts; misses copied from the host stores
+  const int64_t sg = entry_stride(cache->gate), su = entry_stride(cache->up),
+                sd = entry_stride(cache->down);
+  s = cache_map(cache, host_idx, T * top_k, host_slots, [&](int32_t ex, int32_t v) {
+    const struct {
+      void* dst;
+      const void* src;
+      int64_t n;
+    } cp[3] = {
+        {static_cast<uint8_t*>(cache->gate.data) + v * sg,
+         static_cast<const uint8_t*>(cache->host_gate) + ex * sg, sg},
+        {static_cast<uint8_t*>(cache->up.data) + v * su,
+         static_cast<const uint8_t*>(cache->host_up) + ex * su, su},
+        {static_cast<uint8_t*>(cache->down.data) + v * sd,
+         static_cast<const uint8_t*>(cache->host_down) + ex * sd, sd}};
+    for (const auto& c : cp) {
+      const hipError_t ce = hipMemcpyAsync(c.dst, c.src, size_t(c.n), hipMemcpyHostToDevice, st);
+      if (ce != hipSuccess) return hip_status(ce);
+      cache->bytes_copied += uint64_t(c.n);
+    }
+    return DSQ_OK;
+  });
+  if (s != DSQ_OK) return s;
+  DSQ_TRY(hipMemcpyAsync(slots_dev, host_slots, nb, hipMemcpyHostToDevice, st));
+#undef DSQ_TRY
+  // (4) the expert FFN on the slots, routing given
+  return run_moe(X, nullptr, 0.0f, nullptr, nullptr, router_w, bias, cache->gate, cache->up,
+                 cache->down, T, top_k, use_bf16(math, T), Y, moe_ws, nullptr, nullptr, nullptr,
+                 nullptr, slots_dev, w, st);
 }
 
 }  // extern "C"

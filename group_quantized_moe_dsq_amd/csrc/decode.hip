@@ -165,9 +165,9 @@ struct DecArgs {
   int64_t d_stride, d_meta_off;    // down entry geometry (N = H, K = I)
   int H, I, group, k, E;
   const float* X;        // [T][H]
-  const float* logits;   // [T][E] router scores (bias included)
-  int32_t* idx;          // [T][k] written by the gate/up kernel
-  float* w;              // [T][k] written by the gate/up kernel
+  const float* logits;   // [T][E] router scores (bias included), or NULL: routing given
+  int32_t* idx;          // [T][k] written by the gate/up kernel (read when given)
+  float* w;              // [T][k] written by the gate/up kernel (read when given)
   float* hbuf;           // [T*k][I]
   float* Y;              // [T][H]
   const float* resid;    // [T][H] added to Y, or NULL (may equal Y)
@@ -509,11 +509,17 @@ __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
   // loads are in flight; waves 0..T-1 rank the tokens' scores meanwhile
   StageRegs x0;
   stage_load(p.X, H, nullptr, 1, H, threadIdx.x, 512, x0);
-  if (wv < T)
-    topk_all<kDecodeMaxE / 64>(p.logits + int64_t(wv) * p.E, p.E, k, lane, s_e + wv * k,
-                               s_w + wv * k);
+  if (p.logits) {
+    if (wv < T)
+      topk_all<kDecodeMaxE / 64>(p.logits + int64_t(wv) * p.E, p.E, k, lane, s_e + wv * k,
+                                 s_w + wv * k);
+  } else if (threadIdx.x < T * k) {
+    // routing given by the caller (idx/w already in memory)
+    s_e[threadIdx.x] = p.idx[threadIdx.x];
+    s_w[threadIdx.x] = p.w[threadIdx.x];
+  }
   __syncthreads();
-  if (blockIdx.x == 0 && threadIdx.x < T * k) {
+  if (p.logits && blockIdx.x == 0 && threadIdx.x < T * k) {
     p.idx[threadIdx.x] = s_e[threadIdx.x];
     p.w[threadIdx.x] = s_w[threadIdx.x];
   }

@@ -64,7 +64,8 @@ hipError_t launch_router_gemv(const float* X, int64_t T, const float* Wr, const 
                               float* xn, hipStream_t stream);
 constexpr int64_t kDecodeMaxTokens = 4;  // decode kernels: at most this many tokens
 bool decode_supported(int bits, int64_t H, int64_t I, int32_t E, int32_t k);
-// Ranks each token's scores itself (writing idx/w), so no separate top-k.
+// Ranks each token's scores itself (writing idx/w), so no separate top-k;
+// with logits NULL the routing idx/w is read as given.
 hipError_t launch_moe_decode(const dsq_qweight& gate, const dsq_qweight& up,
                              const dsq_qweight& down, const float* X, int64_t T, int32_t E,
                              int32_t k, const float* logits, int32_t* idx, float* w, float* hbuf,

@@ -10,6 +10,7 @@ from __future__ import annotations
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,7 +27,9 @@ LAYOUT_VERSION = 1
 EXPORTS = ["dsq_status_string", "dsq_packed_bytes", "dsq_qweight_init", "dsq_pack_weights",
            "dsq_gemv", "dsq_gemm_workspace_bytes", "dsq_gemm", "dsq_moe_route_topk",
            "dsq_moe_workspace_bytes", "dsq_moe_ffn", "dsq_topk_workspace_bytes", "dsq_topk",
-           "dsq_gemv_topk", "dsq_moe_block_workspace_bytes", "dsq_moe_block"]
+           "dsq_gemv_topk", "dsq_moe_block_workspace_bytes", "dsq_moe_block",
+           "dsq_expert_cache_init", "dsq_expert_cache_plan", "dsq_moe_cached_workspace_bytes",
+           "dsq_moe_ffn_cached"]
 
 
 class DsqError(RuntimeError):
@@ -40,6 +43,16 @@ class QWeightDesc(ctypes.Structure):
                 ("N", ctypes.c_int64), ("batch", ctypes.c_int64),
                 ("layout_version", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
                 ("data", ctypes.c_void_p)]
+
+
+class ExpertCacheDesc(ctypes.Structure):
+    _fields_ = [("gate", QWeightDesc), ("up", QWeightDesc), ("down", QWeightDesc),
+                ("host_gate", ctypes.c_void_p), ("host_up", ctypes.c_void_p),
+                ("host_down", ctypes.c_void_p), ("E", ctypes.c_int32), ("slots", ctypes.c_int32),
+                ("slot_of", ctypes.c_void_p), ("expert_of", ctypes.c_void_p),
+                ("last_use", ctypes.c_void_p), ("clock", ctypes.c_uint64),
+                ("hits", ctypes.c_uint64), ("misses", ctypes.c_uint64),
+                ("bytes_copied", ctypes.c_uint64)]
 
 
 _lib = None
@@ -81,6 +94,16 @@ def lib():
         L.dsq_moe_block.argtypes = [vp, vp, ctypes.c_float, vp, vp, pd, pd, pd, i64, i32, i32, vp,
                                     vp, sz, vp, vp, vp, vp, vp, vp]
         L.dsq_moe_block.restype = i32
+        pc = ctypes.POINTER(ExpertCacheDesc)
+        L.dsq_expert_cache_init.argtypes = [pc, pd, pd, pd, vp, vp, vp, i32, vp, vp, vp]
+        L.dsq_expert_cache_init.restype = i32
+        L.dsq_expert_cache_plan.argtypes = [pc, vp, i64, vp, vp, vp, vp]
+        L.dsq_expert_cache_plan.restype = i32
+        L.dsq_moe_cached_workspace_bytes.argtypes = [i64, i32, i32, i32, i64, i64, i32]
+        L.dsq_moe_cached_workspace_bytes.restype = sz
+        L.dsq_moe_ffn_cached.argtypes = [vp, vp, vp, pc, i64, i32, i32, vp, vp, sz, vp, vp, vp, vp,
+                                         vp, vp]
+        L.dsq_moe_ffn_cached.restype = i32
         L.dsq_topk_workspace_bytes.argtypes = [i64, i32]
         L.dsq_topk_workspace_bytes.restype = sz
         L.dsq_topk.argtypes = [vp, i64, i32, vp, vp, vp, sz, vp]
@@ -306,4 +329,92 @@ def moe_block(layer: MoeLayer, X: torch.Tensor, norm_w: torch.Tensor, eps: float
                                workspace.numel() - off, _ptr(xn_out), _ptr(logits_out),
                                _ptr(idx_out), _ptr(w_out), _ptr(counts_out), _stream(stream)),
            "dsq_moe_block")
+    return Y
+
+
+class ExpertCache:
+    """Host-resident experts streamed into `slots` HBM slots, least recently
+    used out.  The host stores hold E packed entries of each matrix in pinned
+    memory (fill them with store()); the tables live in numpy arrays owned
+    here.  Counters: hits, misses (requests), bytes_copied."""
+
+    def __init__(self, bits: int, group: int, H: int, I: int, E: int, slots: int,
+                 device="cuda", pinned: bool = True):
+        self.gate = QWeight(bits, group, H, I, slots, device=device)
+        self.up = QWeight(bits, group, H, I, slots, device=device)
+        self.down = QWeight(bits, group, I, H, slots, device=device)
+        self.E, self.slots, self.H, self.I = E, slots, H, I
+        self.strides = [packed_bytes(bits, group, H, I), packed_bytes(bits, group, H, I),
+                        packed_bytes(bits, group, I, H)]
+        self.host = [torch.empty(E * st, dtype=torch.uint8, pin_memory=pinned)
+                     for st in self.strides]
+        self.slot_of = np.full(E, -1, np.int32)
+        self.expert_of = np.full(slots, -1, np.int32)
+        self.last_use = np.zeros(slots, np.uint64)
+        self.desc = ExpertCacheDesc()
+        _check(lib().dsq_expert_cache_init(
+            ctypes.byref(self.desc), ctypes.byref(self.gate.desc), ctypes.byref(self.up.desc),
+            ctypes.byref(self.down.desc), ctypes.c_void_p(self.host[0].data_ptr()),
+            ctypes.c_void_p(self.host[1].data_ptr()), ctypes.c_void_p(self.host[2].data_ptr()), E,
+            self.slot_of.ctypes.data, self.expert_of.ctypes.data, self.last_use.ctypes.data),
+            "dsq_expert_cache_init")
+
+    def store(self, e: int, wg: torch.Tensor, wu: torch.Tensor, wd: torch.Tensor):
+        """Pack expert e's fp32 weights (on the GPU) into the host stores."""
+        for m, (w, src) in enumerate(((wg, self.gate), (wu, self.up), (wd, self.down))):
+            q = QWeight(src.bits, src.group, src.K, src.N, 1, device=w.device)
+            pack_weights(w.contiguous(), q)
+            st = self.strides[m]
+            self.host[m][e * st:(e + 1) * st].copy_(q.buf[:st])
+
+    def plan(self, experts: np.ndarray):
+        """Host-only slot mapping of one call: (slots, fill_experts, fill_slots)."""
+        ex = np.ascontiguousarray(experts, np.int32).reshape(-1)
+        n = ex.size
+        so, fe, fs = (np.empty(max(n, 1), np.int32) for _ in range(3))
+        nf = ctypes.c_int64(0)
+        _check(lib().dsq_expert_cache_plan(ctypes.byref(self.desc), ex.ctypes.data, n,
+                                           so.ctypes.data, fe.ctypes.data, fs.ctypes.data,
+                                           ctypes.byref(nf)), "dsq_expert_cache_plan")
+        return so[:n], fe[:nf.value], fs[:nf.value]
+
+    @property
+    def hits(self):
+        return int(self.desc.hits)
+
+    @property
+    def misses(self):
+        return int(self.desc.misses)
+
+    @property
+    def bytes_copied(self):
+        return int(self.desc.bytes_copied)
+
+
+def moe_cached_workspace_bytes(T, E, slots, top_k, H, I, math) -> int:
+    return int(lib().dsq_moe_cached_workspace_bytes(T, E, slots, top_k, H, I, math))
+
+
+def moe_ffn_cached(router_w: torch.Tensor, bias, cache: ExpertCache, X: torch.Tensor, top_k: int,
+                   math: int = MATH_AUTO, Y=None, workspace=None, logits_out=None, idx_out=None,
+                   w_out=None, stream=None):
+    """One MoE layer with its experts behind `cache` (synchronises the stream
+    once: the host must see the routing)."""
+    _need(X, torch.float32, "X")
+    T = X.shape[0]
+    if Y is None:
+        Y = torch.empty((T, cache.H), dtype=torch.float32, device=X.device)
+    need = moe_cached_workspace_bytes(T, cache.E, cache.slots, top_k, cache.H, cache.I, math)
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=X.device)
+    off = (-workspace.data_ptr()) % 256
+    host_idx = np.empty(max(T * top_k, 1), np.int32)
+    host_slots = np.empty(max(T * top_k, 1), np.int32)
+    _check(lib().dsq_moe_ffn_cached(_ptr(X), _ptr(router_w), _ptr(bias), ctypes.byref(cache.desc),
+                                    T, top_k, math, _ptr(Y),
+                                    ctypes.c_void_p(workspace.data_ptr() + off),
+                                    workspace.numel() - off, host_idx.ctypes.data,
+                                    host_slots.ctypes.data, _ptr(logits_out), _ptr(idx_out),
+                                    _ptr(w_out), _stream(stream)), "dsq_moe_ffn_cached")
+    cache.last_slots = host_slots[:T * top_k].reshape(T, top_k)
     return Y

@@ -23,9 +23,10 @@
  *
  * Conventions shared by every call:
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
- *     allocates nothing, keeps no state between calls and never synchronises;
- *     every call only enqueues kernels on `stream` (a hipStream_t, NULL = the
- *     default stream).  Calls are re-entrant; two calls that share a
+ *     allocates nothing, keeps no state between calls (the expert cache keeps
+ *     its state in caller-owned tables) and never synchronises (except
+ *     dsq_moe_ffn_cached, whose host must see the routing); every call only
+ *     enqueues work on `stream` (a hipStream_t, NULL = the default stream).  Calls are re-entrant; two calls that share a
  *     workspace must be ordered on one stream.
  *   - Arguments are validated on the host before anything is enqueued.  A
  *     failed check returns a negative dsq_status and enqueues nothing, so no
@@ -305,6 +306,95 @@ dsq_status dsq_moe_block(const float* X, const float* norm_w, float eps, const f
                          float* Y, void* workspace, size_t workspace_bytes, float* xn_out,
                          float* logits_out, int32_t* idx_out, float* w_out,
                          int32_t* expert_counts_out, void* stream);
+
+/*
+ * Expert cache: host-resident experts streamed into HBM slots, least
+ * recently used first out ("Running a 284B-parameter LLM from 3.2 GB of RAM
+ * in plain C": per token the router decides which experts are needed and
+ * only those are read into an LRU cache; a larger cache hits more often, and
+ * a cache smaller than one step's set of experts never hits).  Here the
+ * store is host memory and the cache lives in HBM; a miss is one host-to-
+ * device copy of the expert's three packed matrices.
+ *
+ * All state sits in caller-owned memory; the library allocates nothing.
+ *   gate, up, down : the device slots, descriptors of packed weights with
+ *                    batch = slots (as for dsq_moe_ffn: N = I, K = H for
+ *                    gate/up, N = H, K = I for down; shared bits and group).
+ *   host_gate, host_up, host_down : host stores of E packed entries each,
+ *                    entry e at e * (the matrix's per-entry stride, i.e.
+ *                    dsq_packed_bytes(bits, group, K, N, 1)), bytes exactly
+ *                    as dsq_pack_weights lays out one entry.  Pinned memory
+ *                    (hipHostMalloc) makes the copies asynchronous.
+ *   slot_of [E], expert_of [slots], last_use [slots] : host tables.
+ * Counters: hits and misses count requests (one per routing entry);
+ * bytes_copied the host-to-device bytes of the misses.
+ */
+typedef struct dsq_expert_cache {
+  dsq_qweight gate, up, down;  /* device slots (batch = slots)                */
+  const void* host_gate;       /* host stores, E entries each                 */
+  const void* host_up;
+  const void* host_down;
+  int32_t E;                   /* experts in the stores                       */
+  int32_t slots;               /* = gate.batch                                */
+  int32_t* slot_of;            /* [E]: slot holding expert e, or -1           */
+  int32_t* expert_of;          /* [slots]: expert in slot s, or -1            */
+  uint64_t* last_use;          /* [slots]: call stamp of the last use         */
+  uint64_t clock;              /* calls so far                                */
+  uint64_t hits, misses, bytes_copied;
+} dsq_expert_cache;
+
+/* Fill a cache over the given slots, stores and tables; every slot starts
+   empty.  Errors: DSQ_ERR_INVALID_ARG (NULL pointer, E < 1), DSQ_ERR_SHAPE
+   (slot descriptors that do not form one MoE layer), and the descriptor
+   errors of dsq_moe_ffn. */
+dsq_status dsq_expert_cache_init(dsq_expert_cache* cache, const dsq_qweight* gate,
+                                 const dsq_qweight* up, const dsq_qweight* down,
+                                 const void* host_gate, const void* host_up,
+                                 const void* host_down, int32_t E, int32_t* slot_of,
+                                 int32_t* expert_of, uint64_t* last_use);
+
+/*
+ * dsq_expert_cache_plan -- host only, no GPU call: map n requested experts
+ * (host [n]) to slots (slot_out host [n]) as one call.  A requested expert
+ * already in a slot is a hit; a miss takes an empty slot (lowest index)
+ * or else the least recently used slot not used in this call (ties: lowest
+ * index), and is reported in fill_expert/fill_slot (host [n] each, *n_fill
+ * entries written, in request order).  Errors: DSQ_ERR_INVALID_ARG (NULL,
+ * n < 0, an expert out of 0..E-1), DSQ_ERR_UNSUPPORTED (one call needs more
+ * distinct experts than there are slots; the tables stay consistent, the
+ * entries before the failing one are mapped).
+ */
+dsq_status dsq_expert_cache_plan(dsq_expert_cache* cache, const int32_t* experts, int64_t n,
+                                 int32_t* slot_out, int32_t* fill_expert, int32_t* fill_slot,
+                                 int64_t* n_fill);
+
+/* Bytes of workspace for dsq_moe_ffn_cached: 0 if the arguments are invalid. */
+size_t dsq_moe_cached_workspace_bytes(int64_t T, int32_t E, int32_t slots, int32_t top_k,
+                                      int64_t H, int64_t I, int32_t math);
+
+/*
+ * dsq_moe_ffn_cached -- dsq_moe_ffn with the experts behind an expert cache:
+ *   route on the GPU (fp32 router logits with the bias, softmax + top-k +
+ *   renormalisation as dsq_moe_route_topk), copy the routing to the host and
+ *   SYNCHRONISE the stream (the one call of the library that does: the host
+ *   must see the routing to fetch experts), map the requested experts to
+ *   slots as dsq_expert_cache_plan and enqueue the copies of the misses,
+ *   then run the expert FFN of dsq_moe_ffn on the slots.
+ *   router_w : fp32 [E][H] device (E = cache->E); bias fp32 [E] or NULL.
+ *   host_idx, host_slots : host [T][k] int32 scratch (the routing and its
+ *            slots); host_slots must stay valid until the stream reaches
+ *            this call's end.
+ *   workspace: dsq_moe_cached_workspace_bytes(T, E, slots, top_k, H, I, math).
+ *   Optional outputs: logits_out fp32 [T][E], idx_out int32 [T][k] (expert
+ *   ids), w_out fp32 [T][k], all device.
+ * Limits as dsq_moe_ffn, plus T*top_k distinct experts fit the slots.
+ * Errors as dsq_moe_ffn and dsq_expert_cache_plan.
+ */
+dsq_status dsq_moe_ffn_cached(const float* X, const float* router_w, const float* bias,
+                              dsq_expert_cache* cache, int64_t T, int32_t top_k, int32_t math,
+                              float* Y, void* workspace, size_t workspace_bytes,
+                              int32_t* host_idx, int32_t* host_slots, float* logits_out,
+                              int32_t* idx_out, float* w_out, void* stream);
 
 #ifdef __cplusplus
 }
