@@ -25,7 +25,10 @@
 namespace dsq {
 
 #ifndef DSQ_GEMV_SB_R
-#define DSQ_GEMV_SB_R 4  // rows per wave step
+#define DSQ_GEMV_SB_R 2  // rows per wave step
+#endif
+#ifndef DSQ_GEMV_SB_BUFS
+#define DSQ_GEMV_SB_BUFS 3  // row blocks in flight per wave (2 or 3)
 #endif
 
 // (S, M) of sub-block j from its block's header: x = d | dmin << 16 (fp16
@@ -149,6 +152,33 @@ __global__ __launch_bounds__(256) void gemv_sb4_kernel(const uint8_t* __restrict
   };
 
   extern __shared__ float4 xl[];
+#if DSQ_GEMV_SB_BUFS == 3
+  // Three buffers: a row block's loads are issued two steps before its
+  // arithmetic.  Loads past the last row block re-read the last row (clamped
+  // addresses), so every load is unconditional and the waits stay static.
+  SbRowChunks<R, KCH> A, B, C;
+  int rb = wave;
+  load(A, rb);
+  load(B, rb + nwaves);
+  // every thread takes its share of x, so a wave without rows leaves only
+  // after the barrier
+  stage_lds<8>(x, K, xl);
+  __syncthreads();
+  if (rb * R >= N) return;
+  xs.load_lds(xl, nchunk, lane);
+  xs.sums();
+  for (;; rb += 3 * nwaves) {
+    load(C, rb + 2 * nwaves);
+    finish(A, rb);
+    if ((rb + nwaves) * R >= N) break;
+    load(A, rb + 3 * nwaves);
+    finish(B, rb + nwaves);
+    if ((rb + 2 * nwaves) * R >= N) break;
+    load(B, rb + 4 * nwaves);
+    finish(C, rb + 2 * nwaves);
+    if ((rb + 3 * nwaves) * R >= N) break;
+  }
+#else
   SbRowChunks<R, KCH> A, B;
   int rb = wave;
   if (rb * R < N) load(A, rb);
@@ -167,6 +197,7 @@ __global__ __launch_bounds__(256) void gemv_sb4_kernel(const uint8_t* __restrict
     finish(B, rb1);
     rb = rb2;
   }
+#endif
 }
 
 // Rows longer than 4 chunks per lane (K > 8192): x is re-read from memory
