@@ -174,6 +174,29 @@ def test_moe_block_validation_and_workspace_query():
     assert dsq.moe_block_workspace_bytes(5, E, 9, H, I, 0) == 0
 
 
+def test_empty_token_batches_return_ok_without_a_device():
+    # T = 0 is valid for the MoE entry points: nothing is enqueued
+    L = dsq.lib()
+    H, I, E = 256, 128, 8
+    g, _ = desc(4, 64, H, I, E)
+    u, _ = desc(4, 64, H, I, E)
+    dn, _ = desc(4, 64, I, H, E)
+    fake = ctypes.c_void_p(0x40000)
+    need = dsq.moe_block_workspace_bytes(0, E, 2, H, I, 0)
+    assert need > 0
+    assert L.dsq_moe_block(fake, fake, 1e-6, fake, None, ctypes.byref(g), ctypes.byref(u),
+                           ctypes.byref(dn), 0, 2, 0, fake, fake, need, None, None, None, None,
+                           None, None) == 0
+    assert L.dsq_moe_ffn(fake, fake, None, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), 0,
+                         2, 0, fake, fake, dsq.moe_workspace_bytes(0, E, 2, H, I, 0), None, None,
+                         None, None, None) == 0
+    c = dsq.ExpertCache(4, 64, H, I, 32, 8, device="cpu", pinned=False)
+    need = dsq.moe_cached_workspace_bytes(0, 32, 8, 2, H, I, 0)
+    assert L.dsq_moe_ffn_cached(fake, fake, None, ctypes.byref(c.desc), 0, 2, 0, fake, fake, need,
+                                None, None, None, None, None, None) == 0
+    assert c.hits == c.misses == 0 and (c.expert_of == -1).all()
+
+
 def test_layout_decoder_round_trip():
     """The test-side layout reader inverts its own encoder, and the encoder
     puts INT4 codes where the header says (word j, byte i: k = 8j+i low,
