@@ -122,9 +122,142 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same logits on the fp32 matrix cores (v_mfma_f32_16x16x4_f32, fp32
+// products and sums).  A workgroup of NW waves owns a tile of 16 tokens x 16
+// experts; wave w takes the part w of K.  Within a wave, the K range is
+// walked in chunks of 16: lane group g (16 lanes) holds elements 4g .. 4g+3 of
+// a chunk and MFMA u of the chunk takes element 4g + u from group g, for A
+// (tokens) and B (experts) alike; the four groups of a row read 64 contiguous
+// bytes per instruction.  Lane l supplies
+// A[token l%16] and B[expert l%16]; its 4 results are tokens 4(l/16) .. +3 of
+// expert l%16.  The waves' partial tiles meet in LDS in a fixed order.
+// Requires K % (256 NW) == 0 (whole stages of 64 k per wave, four stages).
+// ---------------------------------------------------------------------------
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+#ifndef DSQ_ROUTER_NW
+#define DSQ_ROUTER_NW 4  // waves per workgroup = ways K is split
+#endif
+constexpr int kRouterNW = DSQ_ROUTER_NW;
+
+__global__ __launch_bounds__(64 * kRouterNW) void router_mfma_kernel(RouterArgs p) {
+  __shared__ f32x4v part[kRouterNW][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  // tile of this workgroup; workgroup b runs on XCD b % 8: when the tile grid
+  // splits evenly, XCD x takes one block of (tiles_t / 2) x (tiles_e / 4)
+  // tiles, so its L2 sees a quarter of the weights and half of the tokens
+  const int tiles_e = (p.N + 15) / 16;
+  const int tiles_t = int((p.M + 15) / 16);
+  const int blk = blockIdx.x;
+  int te, tt;
+  if (tiles_t % 2 == 0 && tiles_e % 4 == 0) {
+    const int x = blk % 8, i = blk / 8;
+    const int bw = tiles_e / 4;  // block width in expert tiles
+    te = (x % 4) * bw + i % bw;
+    tt = (x / 4) * (tiles_t / 2) + i / bw;
+  } else {
+    te = blk % tiles_e;
+    tt = blk / tiles_e;
+  }
+  const int e0 = te * 16;
+  const int64_t t0 = int64_t(tt) * 16;
+  const int K = p.K, KQ = K / kRouterNW;  // K range per wave
+  const int64_t tr = t0 + r16 < p.M ? t0 + r16 : p.M - 1;  // clamped rows: loads stay in range
+  const int er = e0 + r16 < p.N ? e0 + r16 : p.N - 1;
+  // lane group g holds elements 4g .. 4g+3 of every 16-element chunk of the
+  // wave's K range: the four groups of a row read one contiguous 64 bytes
+  const float4* xa = reinterpret_cast<const float4*>(p.X + tr * K + wv * KQ) + g;
+  const float4* wb = reinterpret_cast<const float4*>(p.W + int64_t(er) * K + wv * KQ) + g;
+  f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+  // chunks of 4 float4 per operand (16 MFMAs); four register stages, loads
+  // three chunks ahead.  Chunk indices past the end are clamped, so every
+  // load is unconditional and the compiler's waits stay static.
+  const int nch = KQ / 64;  // stages of 4 chunks; a multiple of 4 (K % (256 NW) == 0)
+  float4 a[4][4], b[4][4];
+  auto load = [&](float4 (&av)[4], float4 (&bv)[4], int c) {
+    const int cc = c < nch ? c : nch - 1;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      av[u] = xa[(cc * 4 + u) * 4];
+      bv[u] = wb[(cc * 4 + u) * 4];
+    }
+  };
+  auto mma = [&](const float4 (&av)[4], const float4 (&bv)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u].x, bv[u].x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u].y, bv[u].y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u].z, bv[u].z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u].w, bv[u].w, acc, 0, 0, 0);
+    }
+  };
+  // (the scheduling barriers keep each stage's loads where they are issued:
+  // left alone, the scheduler sinks every load to just before its use)
+  load(a[0], b[0], 0);
+  load(a[1], b[1], 1);
+  load(a[2], b[2], 2);
+  for (int c = 0; c < nch; c += 4) {
+    load(a[3], b[3], c + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a[0], b[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    load(a[0], b[0], c + 4);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a[1], b[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    load(a[1], b[1], c + 5);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a[2], b[2]);
+    __builtin_amdgcn_sched_barrier(0);
+    load(a[2], b[2], c + 6);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a[3], b[3]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  part[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0) {
+    f32x4v v = part[0][lane];
+#pragma unroll
+    for (int w = 1; w < kRouterNW; ++w) v += part[w][lane];
+    const int e = e0 + r16;
+    if (e < p.N) {
+      const float b = p.bias ? p.bias[e] : 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t t = t0 + 4 * g + q;
+        if (t < p.M) p.out[t * p.N + e] = p.bias ? v[q] + b : v[q];
+      }
+    }
+  }
+}
+
+#ifndef DSQ_ROUTER_R
+#define DSQ_ROUTER_R 2   // experts per wave
+#endif
+#ifndef DSQ_ROUTER_MT
+#define DSQ_ROUTER_MT 8  // tokens per tile
+#endif
+
 hipError_t launch_router(const float* X, int64_t T, const float* Wr, const float* bias,
                          int32_t E, int64_t H, float* logits, hipStream_t stream) {
-  constexpr int R = 2, MT = 8;
+  if (H % (256 * kRouterNW) == 0 && ((E + 15) / 16) * ((T + 15) / 16) <= int64_t(INT32_MAX)) {
+    RouterArgs a{};
+    a.W = Wr;
+    a.N = E;
+    a.K = int(H);
+    a.X = X;
+    a.M = T;
+    a.out = logits;
+    a.bias = bias;
+    if (T == 0 || E == 0) return hipSuccess;
+    hipLaunchKernelGGL(router_mfma_kernel, dim3(unsigned(((E + 15) / 16) * ((T + 15) / 16))),
+                       dim3(64 * kRouterNW), 0, stream, a);
+    return hipGetLastError();
+  }
+  constexpr int R = DSQ_ROUTER_R, MT = DSQ_ROUTER_MT;
   RouterArgs a{};
   a.W = Wr;
   a.N = E;
