@@ -30,6 +30,14 @@ namespace dsq {
 #ifndef DSQ_GEMV_SB_BUFS
 #define DSQ_GEMV_SB_BUFS 3  // row blocks in flight per wave (2 or 3)
 #endif
+#ifndef DSQ_GEMV_SB_FENCE
+#define DSQ_GEMV_SB_FENCE 1  // keep each buffer's loads ahead of the arithmetic (57.5 against 59.4 us)
+#endif
+#if DSQ_GEMV_SB_FENCE
+#define SB_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+#else
+#define SB_SCHED_FENCE() ((void)0)
+#endif
 
 // (S, M) of sub-block j from its block's header: x = d | dmin << 16 (fp16
 // bits), then the 96 bits of 6-bit fields sc_0..7, m_0..7 (field f at bit 6f).
@@ -169,12 +177,15 @@ __global__ __launch_bounds__(256) void gemv_sb4_kernel(const uint8_t* __restrict
   xs.sums();
   for (;; rb += 3 * nwaves) {
     load(C, rb + 2 * nwaves);
+    SB_SCHED_FENCE();
     finish(A, rb);
     if ((rb + nwaves) * R >= N) break;
     load(A, rb + 3 * nwaves);
+    SB_SCHED_FENCE();
     finish(B, rb + nwaves);
     if ((rb + 2 * nwaves) * R >= N) break;
     load(B, rb + 4 * nwaves);
+    SB_SCHED_FENCE();
     finish(C, rb + 2 * nwaves);
     if ((rb + 3 * nwaves) * R >= N) break;
   }
