@@ -98,6 +98,9 @@ struct MoeWs {
   size_t act_bytes;
   float* xs;         // their per-group sums
   size_t xs_bytes;
+  int4* tiles;       // token-tile table of the grouped GEMM
+  int32_t* n_tiles;
+  int64_t max_tiles;
 };
 
 int64_t moe_layout(void* ws, int64_t T, int32_t E, int32_t k, int64_t H, int64_t I, int group,
@@ -125,6 +128,9 @@ int64_t moe_layout(void* ws, int64_t T, int32_t E, int32_t k, int64_t H, int64_t
   m.act = c.take(int64_t(m.act_bytes), 1);
   m.xs_bytes = gmm_xs_bytes(nk, segs, xp, kmax, group);
   m.xs = static_cast<float*>(c.take(int64_t(m.xs_bytes), 1));
+  m.max_tiles = gmm_tiles_bound(nk, segs, xp);
+  m.tiles = static_cast<int4*>(c.take(m.max_tiles, 16));
+  m.n_tiles = static_cast<int32_t*>(c.take(1, 4));
   // the grouped GEMM addresses these with 32-bit offsets
   if (m.act_bytes > size_t(INT32_MAX) || m.xs_bytes > size_t(INT32_MAX)) c.overflow = true;
   if (out) *out = m;
@@ -383,7 +389,7 @@ dsq_status run_moe(const float* X, const float* gamma, float eps, float* xn, con
                               m.w, static_cast<float*>(m.hbuf), Y, resid, st));
     if (expert_counts_out) {
       DSQ_TRY(launch_group(m.idx, T, top_k, E, m.bitmap, m.counts, m.offsets, m.perm, m.pos,
-                           m.active, m.n_active, st));
+                           m.active, m.n_active, 0, nullptr, nullptr, st));
     }
     return DSQ_OK;
   }
@@ -398,9 +404,10 @@ dsq_status run_moe(const float* X, const float* gamma, float eps, float* xn, con
     // (2) softmax + top-k + renormalisation
     DSQ_TRY(launch_topk(m.logits, nullptr, T, E, top_k, m.idx, m.w, st));
   }
-  // (3) stable grouping by expert
+  // (3) stable grouping by expert, and the token tiles of the grouped GEMMs
+  const int xp = bf16 ? 1 : 2;
   DSQ_TRY(launch_group(m.idx, T, top_k, E, m.bitmap, m.counts, m.offsets, m.perm, m.pos, m.active,
-                       m.n_active, st));
+                       m.n_active, 16 / xp, m.tiles, m.n_tiles, st));
   Groups g{};
   g.active = m.active;
   g.n_active = m.n_active;
@@ -409,8 +416,10 @@ dsq_status run_moe(const float* X, const float* gamma, float eps, float* xn, con
   g.top_k = top_k;
   const int64_t max_items = T * top_k < E64 ? T * top_k : E64;
   g.max_items = int32_t(max_items);
+  g.tiles = m.tiles;
+  g.n_tiles = m.n_tiles;
+  g.max_tiles = int32_t(m.max_tiles);
   // (4) expert FFNs over their token groups, (5) weighted combine (+ residual)
-  const int xp = bf16 ? 1 : 2;
   float* hbuf = static_cast<float*>(m.hbuf);
   DSQ_TRY(launch_gmm(gate, &up, 0, &g, XR_GATHER, Xe, H, 0, xp, m.act, m.act_bytes, m.xs,
                      m.xs_bytes, hbuf, I, st));

@@ -35,14 +35,16 @@
 // (one weight row: its scale and zero point are the lane's own) and rows
 // 4 (l / 16) + i, i < 4.
 //
-// Work: a workgroup item is one expert and 64 (SwiGLU) or 128 output rows.
-// Each wave streams the codes of its two 16-row tiles (SwiGLU: the gate and
+// Work: a workgroup item is one pass of one token tile of one expert over
+// 128 (SwiGLU: 128 gate and 128 up) or 256 output rows.  Each wave streams the codes of its two 16-row tiles (SwiGLU: the gate and
 // the up tile of the same rows, so silu(g) u is formed in the lane) straight
 // from HBM into its own LDS ring, 128 bytes of every row per step (whole cache
 // lines; a 16-row operand only needs 32 bytes of a row per INT4 group), and
 // the workgroup shares a ring of the token tile's activation fragments.  Three
-// steps are in flight.  Items are dealt to the workgroups in a fixed stride,
-// so every workgroup gets the same count to within one.
+// steps are in flight.  The routing step lists the token tiles of every
+// expert; items are dealt to the workgroups in a fixed stride, so every
+// workgroup runs the same number of passes to within one whatever the
+// routing (an expert with many tokens is many items, not one long one).
 #include "common.h"
 #include "internal.h"
 #include "mfma_util.h"
@@ -154,9 +156,8 @@ struct GmmArgs {
   int64_t meta_off;         // offset of the (scale, zp) table in an entry
   int N, K, group;
   int64_t expert;           // dense mode entry
-  const int32_t* active;    // NULL: dense
-  const int32_t* n_active;
-  const int32_t* offsets;
+  const int4* tiles;        // NULL: dense; else the token-tile table (Groups::tiles)
+  const int32_t* n_tiles;
   int64_t M;                // dense rows
   const uint4* afrag;
   int64_t afrag_bytes;
@@ -164,7 +165,7 @@ struct GmmArgs {
   int64_t xs_bytes;
   float* out;
   int64_t ld_out;
-  int rt;                   // row blocks (items) per expert
+  int rt;                   // row blocks per token tile
 };
 
 // Chunk swizzle of the code tiles in LDS: 16-byte chunk j of row r sits at
@@ -195,22 +196,24 @@ struct GmmShape {
   static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-// Position in a workgroup's sequence of passes: items (expert, ROWS output
-// rows) dealt in a fixed stride, each item's token tiles in order, each tile
-// one pass of MS steps over K.
+// Position in a workgroup's sequence of passes.  An item is one pass: one
+// token tile of one expert against ROWS output rows, MS steps over K.  Items
+// are numbered (tile, row block), the tiles in table order, and dealt in a
+// fixed stride, so every workgroup runs the same number of passes to within
+// one however the tokens fall on the experts.
 struct GmmCursor {
   int j;           // position in the workgroup's item sequence
   int item;        // global item index (>= items: exhausted)
-  int t, ntiles;   // token tile of the item and their count
   int m;           // step within the pass
-  int tb;          // first token tile of the expert
-  int64_t e, p0, M;
+  int atile;       // activation tile
+  int rows;        // token rows of the tile
+  int64_t e, row0; // expert; first output row (perm order, or dense row)
 };
 
 // Item j of this workgroup.  Workgroup b runs on XCD b % 8; the workgroups of
-// one XCD take consecutive items (the row blocks of one or two experts) at
-// the same time, so that XCD's L2 fetches those experts' activation tiles
-// once.  Every workgroup gets the same number of items to within one.
+// one XCD take consecutive items (every row block of one or two token tiles)
+// at the same time, so that XCD's L2 fetches those activation tiles once, and
+// the weight rows of an expert's tiles together.
 __device__ __forceinline__ int gmm_item(int j) {
   const int nb = gridDim.x, b = blockIdx.x;
   if (nb % 8 != 0) return b + j * nb;
@@ -226,25 +229,31 @@ __device__ __forceinline__ int gmm_item(int j) {
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
 template <int XP>
+__device__ __forceinline__ int gmm_items(const GmmArgs& p) {
+  const int tiles = p.tiles ? __builtin_amdgcn_readfirstlane(*(const_i32_ptr)p.n_tiles)
+                            : int((p.M * XP + 15) / 16);
+  return tiles * p.rt;
+}
+
+template <int XP>
 __device__ __forceinline__ void gmm_cursor_load(const GmmArgs& p, int items, GmmCursor& cu) {
+  constexpr int TPT = 16 / XP;
   cu.item = gmm_item(cu.j);
+  cu.m = 0;
   if (cu.item >= items) return;
-  const int a = cu.item / p.rt;
-  if (p.active) {
-    cu.e = __builtin_amdgcn_readfirstlane(((const_i32_ptr)p.active)[a]);
-    const const_i32_ptr off = (const_i32_ptr)p.offsets;
-    cu.p0 = __builtin_amdgcn_readfirstlane(off[cu.e]);
-    cu.M = __builtin_amdgcn_readfirstlane(off[cu.e + 1]) - cu.p0;
-    cu.tb = int(cu.p0 * XP / 16) + a;
+  const int q = cu.item / p.rt;
+  if (p.tiles) {
+    const const_i32_ptr v = (const_i32_ptr)p.tiles + 4 * int64_t(q);
+    cu.e = __builtin_amdgcn_readfirstlane(v[0]);
+    cu.row0 = __builtin_amdgcn_readfirstlane(v[1]);
+    cu.rows = __builtin_amdgcn_readfirstlane(v[2]);
+    cu.atile = __builtin_amdgcn_readfirstlane(v[3]);
   } else {
     cu.e = p.expert;
-    cu.p0 = 0;
-    cu.M = p.M;
-    cu.tb = 0;
+    cu.row0 = int64_t(q) * TPT;
+    cu.rows = int(min(int64_t(TPT), p.M - cu.row0));
+    cu.atile = q;
   }
-  cu.ntiles = int((cu.M * XP + 15) / 16);
-  cu.t = 0;
-  cu.m = 0;
 }
 
 // Advance by one step; returns true when a new item begins.
@@ -252,8 +261,6 @@ template <int XP>
 __device__ __forceinline__ bool gmm_cursor_next(const GmmArgs& p, int items, int MS,
                                                 GmmCursor& cu) {
   if (++cu.m < MS) return false;
-  cu.m = 0;
-  if (++cu.t < cu.ntiles) return false;
   ++cu.j;
   gmm_cursor_load<XP>(p, items, cu);
   return true;
@@ -272,7 +279,6 @@ template <int BITS, int J, int XP, bool SWIGLU>
 __device__ __forceinline__ void gmm_stream(const GmmArgs& p, uint8_t* sm) {
   using Sh = GmmShape<BITS, J, SWIGLU>;
   constexpr int NB = Sh::NB, L = Sh::L, DM = Sh::DM;
-  constexpr int TPT = 16 / XP;  // tokens per tile
   constexpr int LB = J * BITS;  // code bytes per lane, tile and group
   constexpr float kOff = BITS == 4 ? 16.0f : 0.0f;
   static_assert(DM >= 2 && DM <= 4, "waits below");
@@ -285,7 +291,7 @@ __device__ __forceinline__ void gmm_stream(const GmmArgs& p, uint8_t* sm) {
   const int G = p.group, S = p.K / G;
   const int MS = (S + L - 1) / L;  // steps over K
   const int64_t RB = int64_t(p.K) * BITS / 8;
-  const int items = (p.active ? *p.n_active : 1) * p.rt;
+  const int items = gmm_items<XP>(p);
   const __amdgpu_buffer_rsrc_t ra = rsrc(p.afrag, p.afrag_bytes);
   const __amdgpu_buffer_rsrc_t rx = rsrc(p.xs, p.xs_bytes);
   const bool mlane = lane < 16 * Sh::PPR;
@@ -333,7 +339,7 @@ __device__ __forceinline__ void gmm_stream(const GmmArgs& p, uint8_t* sm) {
     uint8_t* ws = wring + slot * Sh::WSLOT;
     uint8_t* as = aring + slot * Sh::ASLOT;
     const int m = la.m;
-    const int tile = la.tb + la.t;
+    const int tile = la.atile;
     const int abase = tile * S * J * 1024, xbase = tile * S * 64;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -421,10 +427,9 @@ __device__ __forceinline__ void gmm_stream(const GmmArgs& p, uint8_t* sm) {
     const int wrow = wrow_of(cu.item);
 #pragma unroll
     for (int q = 0; q < 4 / XP; ++q) {
-      const int64_t mrow = int64_t(cu.t) * TPT + g4 * (4 / XP) + q;
-      if (mrow >= cu.M) continue;
-      const int64_t orow = p.active ? cu.p0 + mrow : mrow;
-      float* o = p.out + orow * p.ld_out;
+      const int mrow = g4 * (4 / XP) + q;
+      if (mrow >= cu.rows) continue;
+      float* o = p.out + (cu.row0 + mrow) * p.ld_out;
       if constexpr (SWIGLU) {
         const int n = wrow + c;
         const float gv = XP == 2 ? y[0][2 * q] + y[0][2 * q + 1] : y[0][q];
@@ -491,8 +496,8 @@ int tiles_bound(int64_t rows, int64_t segments, int xp) {
 }
 
 template <int BITS, int J, int XP, bool SWIGLU>
-hipError_t launch_one(const GmmArgs& a, int max_items, hipStream_t stream) {
-  const int64_t total = int64_t(max_items) * a.rt;
+hipError_t launch_one(const GmmArgs& a, int64_t max_tiles, hipStream_t stream) {
+  const int64_t total = max_tiles * a.rt;
   // one workgroup per CU; every workgroup gets the same number of items to
   // within one
   const int64_t blocks = total < 256 ? total : 256;
@@ -503,7 +508,7 @@ hipError_t launch_one(const GmmArgs& a, int max_items, hipStream_t stream) {
 }
 
 template <int XP>
-hipError_t launch_bits(const GmmArgs& a, int bits, bool swiglu, int max_items,
+hipError_t launch_bits(const GmmArgs& a, int bits, bool swiglu, int64_t max_items,
                        hipStream_t stream) {
   const int J = a.group / 32;
   if (bits == 4 && J == 2)
@@ -520,6 +525,10 @@ hipError_t launch_bits(const GmmArgs& a, int bits, bool swiglu, int max_items,
 }
 
 }  // namespace
+
+int64_t gmm_tiles_bound(int64_t rows, int64_t segments, int xp) {
+  return tiles_bound(rows, segments, xp);
+}
 
 size_t gmm_act_bytes(int64_t rows, int64_t segments, int xp, int64_t K) {
   const int64_t tiles = tiles_bound(rows, segments, xp);
@@ -573,10 +582,11 @@ hipError_t launch_gmm(const dsq_qweight& A, const dsq_qweight* B, int64_t expert
   a.group = A.group;
   a.expert = expert;
   a.M = M;
+  int64_t max_tiles = (M * xp + 15) / 16;
   if (grp) {
-    a.active = grp->active;
-    a.n_active = grp->n_active;
-    a.offsets = grp->offsets;
+    a.tiles = grp->tiles;
+    a.n_tiles = grp->n_tiles;
+    max_tiles = grp->max_tiles;
   }
   a.afrag = static_cast<const uint4*>(act);
   a.afrag_bytes = int64_t(act_bytes);
@@ -586,8 +596,8 @@ hipError_t launch_gmm(const dsq_qweight& A, const dsq_qweight* B, int64_t expert
   a.ld_out = ld_out;
   const int rows = B ? 128 : 256;  // output rows per workgroup item
   a.rt = int((A.N + rows - 1) / rows);
-  if (xp == 2) return launch_bits<2>(a, A.bits, B != nullptr, items, stream);
-  return launch_bits<1>(a, A.bits, B != nullptr, items, stream);
+  if (xp == 2) return launch_bits<2>(a, A.bits, B != nullptr, max_tiles, stream);
+  return launch_bits<1>(a, A.bits, B != nullptr, max_tiles, stream);
 }
 
 }  // namespace dsq

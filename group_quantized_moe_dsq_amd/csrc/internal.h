@@ -27,6 +27,12 @@ struct Groups {
   const int32_t* perm;      // [T*k] entry j = t*k+i in (expert, j) order
   int32_t top_k;
   int32_t max_items;        // grid bound on the number of active experts
+  // token tiles in (active expert, tile) order, one record each:
+  // {expert, first row in perm order, rows in the tile (<= 16 / xp),
+  //  activation tile index}; count in *n_tiles, at most max_tiles
+  const int4* tiles;
+  const int32_t* n_tiles;
+  int32_t max_tiles;
 };
 
 // Where the rows of a grouped GEMM come from:
@@ -41,9 +47,12 @@ hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int32_
                        int32_t* idx, float* w, hipStream_t stream);
 
 // Stable grouping of the T*k routing entries by expert (one workgroup).
+// With tiles, also the token-tile table of the grouped GEMM for tiles of tpt
+// rows (Groups::tiles; at most gmm_tiles_bound(T*k, min(T*k, E), 16/tpt)).
 hipError_t launch_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, uint32_t* bitmap,
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
-                        int32_t* active, int32_t* n_active, hipStream_t stream);
+                        int32_t* active, int32_t* n_active, int tpt, int4* tiles,
+                        int32_t* n_tiles, hipStream_t stream);
 
 // Y[t][n] = (resid[t][n] +) sum_i w[t][i] * ybuf[pos[t*k+i]][n]; Y may be resid
 hipError_t launch_combine(const float* ybuf, const int32_t* pos, const float* w, int64_t T,
@@ -86,6 +95,7 @@ hipError_t launch_gemm_mfma(const dsq_qweight& W, int64_t expert, const float* X
 // gmm_xs_bytes for `rows` routed rows in at most `segments` experts).
 // out rows: dense -> m ; grouped -> p (perm order).  With B (SwiGLU up) the
 // output is silu(x A^T) * (x B^T).
+int64_t gmm_tiles_bound(int64_t rows, int64_t segments, int xp);
 size_t gmm_act_bytes(int64_t rows, int64_t segments, int xp, int64_t K);
 size_t gmm_xs_bytes(int64_t rows, int64_t segments, int xp, int64_t K, int group);
 hipError_t launch_gmm(const dsq_qweight& A, const dsq_qweight* B, int64_t expert,

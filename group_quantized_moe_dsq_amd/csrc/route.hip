@@ -373,9 +373,12 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ perm,
                                                      int32_t* __restrict__ pos,
                                                      int32_t* __restrict__ active,
-                                                     int32_t* __restrict__ n_active) {
+                                                     int32_t* __restrict__ n_active, int tpt,
+                                                     int4* __restrict__ tiles,
+                                                     int32_t* __restrict__ n_tiles) {
   __shared__ int32_t s_off[4097];
   __shared__ int32_t s_act[4097];
+  __shared__ int32_t s_tile[4097];
   const int W = (T + 31) / 32;
   const int nent = T * k;
   for (int i = threadIdx.x; i < E * W; i += blockDim.x) bm[i] = 0u;
@@ -393,41 +396,48 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__
     s_off[e] = c;
   }
   __syncthreads();
-  // exclusive scans of counts and of (count > 0) by wave 0
+  // exclusive scans of counts, of (count > 0) and of token tiles by wave 0
+  const int ntpt = tiles ? tpt : 1;
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     const int per = (E + 63) / 64;
     const int lo = lane * per;
     const int hi = min(lo + per, E);
-    int sc = 0, sa = 0;
+    int sc = 0, sa = 0, st = 0;
     for (int e = lo; e < hi; ++e) {
       sc += s_off[e];
       sa += s_off[e] > 0;
+      st += (s_off[e] + ntpt - 1) / ntpt;
     }
-    int ic = sc, ia = sa;  // inclusive scan across lanes
+    int ic = sc, ia = sa, it = st;  // inclusive scan across lanes
     for (int o = 1; o < 64; o <<= 1) {
       const int uc = __shfl_up(ic, o);
       const int ua = __shfl_up(ia, o);
+      const int ut = __shfl_up(it, o);
       if (lane >= o) {
         ic += uc;
         ia += ua;
+        it += ut;
       }
     }
-    int rc = ic - sc, ra = ia - sa;
+    int rc = ic - sc, ra = ia - sa, rt = it - st;
     for (int e = lo; e < hi; ++e) {
       const int c = s_off[e];
       counts[e] = c;
       s_off[e] = rc;
       s_act[e] = ra;
+      s_tile[e] = rt;
       offsets[e] = rc;
       if (c > 0) active[ra] = e;
       rc += c;
       ra += c > 0;
+      rt += (c + ntpt - 1) / ntpt;
     }
     if (lane == 63) {
       offsets[E] = ic;
       s_off[E] = ic;
       *n_active = ia;
+      if (tiles) *n_tiles = it;
     }
   }
   __syncthreads();
@@ -442,14 +452,24 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__
     const int p = s_off[e] + rank;
     perm[p] = j;
     pos[j] = p;
+    // the entry that opens a token tile writes the tile's record; the
+    // activation tile index is the one the grouped GEMM's prep assigns
+    // (segment start / tpt + active rank + tile)
+    if (tiles && rank % tpt == 0) {
+      const int c = s_off[e + 1] - s_off[e];
+      const int t = rank / tpt;
+      tiles[s_tile[e] + t] = make_int4(e, p, min(tpt, c - rank), s_off[e] / tpt + s_act[e] + t);
+    }
   }
 }
 
 hipError_t launch_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, uint32_t* bitmap,
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
-                        int32_t* active, int32_t* n_active, hipStream_t stream) {
+                        int32_t* active, int32_t* n_active, int tpt, int4* tiles,
+                        int32_t* n_tiles, hipStream_t stream) {
+  if (tiles && tpt <= 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, stream, idx, int(T), k, E, bitmap,
-                     counts, offsets, perm, pos, active, n_active);
+                     counts, offsets, perm, pos, active, n_active, tpt, tiles, n_tiles);
   return hipGetLastError();
 }
 

@@ -12,7 +12,8 @@ from group_quantized_moe_dsq_amd import dsq, synth
 pytestmark = pytest.mark.gpu
 
 FP32_CASES = [(8, 64, 2, 300, 512), (4, 64, 7, 129, 4096), (8, 128, 9, 64, 2048),
-              (4, 128, 31, 100, 384), (8, 64, 33, 257, 1024), (4, 64, 8, 4096, 4096)]
+              (4, 128, 31, 100, 384), (8, 64, 33, 257, 1024), (4, 64, 8, 4096, 4096),
+              (8, 64, 100, 300, 1024)]
 
 
 @pytest.mark.parametrize("bits,group,M,N,K", FP32_CASES)

@@ -55,7 +55,9 @@ def check_moe(fx: MoeFixture, X, k, math, rel, tokens=None):
 # T <= 4 runs the per-slot decode kernels, larger T the expert-grouped ones
 SMALL = [(8, 256, 128, 4, 64, 2, 1), (8, 256, 128, 4, 64, 2, 5), (16, 128, 192, 8, 64, 4, 33),
          (8, 256, 128, 4, 64, 2, 3), (16, 512, 256, 8, 128, 6, 4), (4, 8192, 128, 8, 64, 2, 2),
-         (4, 384, 128, 8, 128, 1, 17), (32, 512, 256, 4, 128, 6, 40)]
+         (4, 384, 128, 8, 128, 1, 17), (32, 512, 256, 4, 128, 6, 40),
+         # ~20 tokens per expert: three token tiles of one expert in flight
+         (4, 256, 128, 8, 64, 2, 40)]
 
 
 @pytest.mark.parametrize("E,H,I,bits,group,k,T", SMALL)
