@@ -63,9 +63,8 @@ struct GmmPrepArgs {
   int xrows;                // XR_DENSE / XR_GATHER / XR_SEGMENT
   const int32_t* perm;
   int top_k;
-  const int32_t* active;    // NULL: dense
-  const int32_t* n_active;
-  const int32_t* offsets;
+  const int4* tiles;        // NULL: dense; else the token-tile table
+  const int32_t* n_tiles;
   int64_t M;                // dense rows
   int K, group;
   uint4* afrag;
@@ -76,20 +75,6 @@ template <int XP>
 __global__ __launch_bounds__(256) void gmm_prep_kernel(GmmPrepArgs p) {
   constexpr int TPT = 16 / XP;     // tokens per tile
   constexpr int SEGS = 256 / TPT;  // 8-wide k segments per block
-  int64_t p0, M;
-  int tb;
-  if (p.active) {
-    const int a = blockIdx.y;
-    if (a >= *p.n_active) return;
-    const int e = p.active[a];
-    p0 = p.offsets[e];
-    M = p.offsets[e + 1] - p0;
-    tb = int(p0 * XP / 16) + a;
-  } else {
-    p0 = 0;
-    M = p.M;
-    tb = 0;
-  }
   const int tok = threadIdx.x / SEGS, seg = threadIdx.x % SEGS;
   const int k = (blockIdx.x * SEGS + seg) * 8;
   // K is a multiple of the group and segments are group-aligned, so the lanes
@@ -98,15 +83,25 @@ __global__ __launch_bounds__(256) void gmm_prep_kernel(GmmPrepArgs p) {
   const int G = p.group, J = G / 32, S = p.K / G;
   const int s = k / G, kk = k % G;
   const int g4 = kk / (8 * J), j = (kk % (8 * J)) / 8;
-  const int ntiles = int((M * XP + 15) / 16);
-  for (int t = 0; t < ntiles; ++t) {
-    const int64_t m = int64_t(t) * TPT + tok;
+  // token tiles: blockIdx.y, blockIdx.y + gridDim.y, ...
+  const int ntiles = p.tiles ? *p.n_tiles : int((p.M * XP + 15) / 16);
+  for (int q = blockIdx.y; q < ntiles; q += gridDim.y) {
+    int64_t row0;
+    int rows, atile;
+    if (p.tiles) {
+      const int4 v = p.tiles[q];
+      row0 = v.y;
+      rows = v.z;
+      atile = v.w;
+    } else {
+      row0 = int64_t(q) * TPT;
+      rows = int(min(int64_t(TPT), p.M - row0));
+      atile = q;
+    }
     float v[8];
-    if (m < M) {
-      int64_t row;
-      if (p.xrows == XR_GATHER) row = p.perm[p0 + m] / p.top_k;
-      else if (p.xrows == XR_SEGMENT) row = p0 + m;
-      else row = m;
+    if (tok < rows) {
+      const int64_t m = row0 + tok;
+      const int64_t row = p.xrows == XR_GATHER ? p.perm[m] / p.top_k : m;
       const float4* q = reinterpret_cast<const float4*>(p.src + row * p.ld_src + k);
       const float4 a = q[0], b = q[1];
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
@@ -135,7 +130,7 @@ __global__ __launch_bounds__(256) void gmm_prep_kernel(GmmPrepArgs p) {
       sh += __shfl_xor(sh, o);
       if constexpr (XP == 2) sl += __shfl_xor(sl, o);
     }
-    const int64_t blk = (int64_t(tb + t) * S + s);
+    const int64_t blk = (int64_t(atile) * S + s);
 #pragma unroll
     for (int part = 0; part < XP; ++part) {
       const int R = tok * XP + part;
@@ -491,6 +486,9 @@ __global__ __launch_bounds__(512) void gmm_kernel(GmmArgs p) {
 
 namespace {
 
+// prep workgroups per K segment (token tiles beyond take further rounds)
+constexpr int64_t kPrepMaxTileBlocks = 4096;
+
 int tiles_bound(int64_t rows, int64_t segments, int xp) {
   return int(rows * xp / 16 + segments + 1);
 }
@@ -555,18 +553,19 @@ hipError_t launch_gmm(const dsq_qweight& A, const dsq_qweight* B, int64_t expert
   pa.afrag = static_cast<uint4*>(act);
   pa.xs = xs;
   pa.M = M;
-  int items = 1;
+  int64_t max_tiles = (M * xp + 15) / 16;
   if (grp) {
     pa.perm = grp->perm;
     pa.top_k = grp->top_k;
-    pa.active = grp->active;
-    pa.n_active = grp->n_active;
-    pa.offsets = grp->offsets;
-    items = grp->max_items;
+    pa.tiles = grp->tiles;
+    pa.n_tiles = grp->n_tiles;
+    max_tiles = grp->max_tiles;
+    if (grp->max_items == 0) return hipSuccess;
   }
-  if (items == 0) return hipSuccess;
+  if (max_tiles == 0) return hipSuccess;
   const int segs = xp == 2 ? 32 : 16;
-  const dim3 pgrid(unsigned((A.K / 8 + segs - 1) / segs), unsigned(items));
+  const dim3 pgrid(unsigned((A.K / 8 + segs - 1) / segs),
+                   unsigned(max_tiles < kPrepMaxTileBlocks ? max_tiles : kPrepMaxTileBlocks));
   if (xp == 2) hipLaunchKernelGGL(gmm_prep_kernel<2>, pgrid, dim3(256), 0, stream, pa);
   else hipLaunchKernelGGL(gmm_prep_kernel<1>, pgrid, dim3(256), 0, stream, pa);
   hipError_t e = hipGetLastError();
@@ -582,11 +581,9 @@ hipError_t launch_gmm(const dsq_qweight& A, const dsq_qweight* B, int64_t expert
   a.group = A.group;
   a.expert = expert;
   a.M = M;
-  int64_t max_tiles = (M * xp + 15) / 16;
   if (grp) {
     a.tiles = grp->tiles;
     a.n_tiles = grp->n_tiles;
-    max_tiles = grp->max_tiles;
   }
   a.afrag = static_cast<const uint4*>(act);
   a.afrag_bytes = int64_t(act_bytes);

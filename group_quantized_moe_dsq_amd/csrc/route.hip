@@ -477,24 +477,42 @@ hipError_t launch_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, uin
 // Weighted combine in slot order (§3.5: weighted sum of the expert outputs),
 // plus the block's residual when `resid` is given (§2.1: the residual is
 // added after the MoE step).  The residual element is read and Y written by
-// the same thread, so Y may be the residual itself.
+// the same thread, so Y may be the residual itself.  Slots are taken eight at
+// a time: their positions and weights are loaded together, then their rows,
+// so a token costs two memory round trips per eight slots, not two per slot.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ybuf,
-                                                      const int32_t* __restrict__ pos,
-                                                      const float* __restrict__ w, int T, int k,
-                                                      int H, const float* resid, float* Y) {
+constexpr int kCombineThreads = 128;
+constexpr int kCombineSlots = 8;
+
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(
+    const float* __restrict__ ybuf, const int32_t* __restrict__ pos, const float* __restrict__ w,
+    int T, int k, int H, const float* resid, float* Y) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;  // float4 index
   const int h4 = H / 4;
   if (i >= int64_t(T) * h4) return;
   const int t = int(i / h4), c = int(i % h4);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < k; ++s) {
-    const float ws = w[t * k + s];
-    const float4 v = reinterpret_cast<const float4*>(ybuf + int64_t(pos[t * k + s]) * H)[c];
-    acc.x = fmaf(ws, v.x, acc.x);
-    acc.y = fmaf(ws, v.y, acc.y);
-    acc.z = fmaf(ws, v.z, acc.z);
-    acc.w = fmaf(ws, v.w, acc.w);
+  for (int s0 = 0; s0 < k; s0 += kCombineSlots) {
+    int ps[kCombineSlots];
+    float ws[kCombineSlots];
+#pragma unroll
+    for (int u = 0; u < kCombineSlots; ++u) {
+      const int s = min(s0 + u, k - 1);
+      ps[u] = pos[t * k + s];
+      ws[u] = w[t * k + s];
+    }
+    float4 v[kCombineSlots];
+#pragma unroll
+    for (int u = 0; u < kCombineSlots; ++u)
+      v[u] = reinterpret_cast<const float4*>(ybuf + int64_t(ps[u]) * H)[c];
+#pragma unroll
+    for (int u = 0; u < kCombineSlots; ++u) {
+      if (s0 + u >= k) break;
+      acc.x = fmaf(ws[u], v[u].x, acc.x);
+      acc.y = fmaf(ws[u], v[u].y, acc.y);
+      acc.z = fmaf(ws[u], v[u].z, acc.z);
+      acc.w = fmaf(ws[u], v[u].w, acc.w);
+    }
   }
   if (resid) {
     const float4 r = reinterpret_cast<const float4*>(resid + int64_t(t) * H)[c];
@@ -511,8 +529,8 @@ hipError_t launch_combine(const float* ybuf, const int32_t* pos, const float* w,
                           hipStream_t stream) {
   const int64_t n = T * (H / 4);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, stream, ybuf,
-                     pos, w, int(T), k, int(H), resid, Y);
+  hipLaunchKernelGGL(combine_kernel, dim3(unsigned((n + kCombineThreads - 1) / kCombineThreads)),
+                     dim3(kCombineThreads), 0, stream, ybuf, pos, w, int(T), k, int(H), resid, Y);
   return hipGetLastError();
 }
 
