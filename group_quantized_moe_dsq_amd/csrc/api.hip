@@ -101,6 +101,7 @@ struct MoeWs {
   int4* tiles;       // token-tile table of the grouped GEMM
   int32_t* n_tiles;
   int64_t max_tiles;
+  float* rparts;     // the router's K slices [ks][T][E] (ks = router_slices > 1)
 };
 
 int64_t moe_layout(void* ws, int64_t T, int32_t E, int32_t k, int64_t H, int64_t I, int group,
@@ -131,6 +132,8 @@ int64_t moe_layout(void* ws, int64_t T, int32_t E, int32_t k, int64_t H, int64_t
   m.max_tiles = gmm_tiles_bound(nk, segs, xp);
   m.tiles = static_cast<int4*>(c.take(m.max_tiles, 16));
   m.n_tiles = static_cast<int32_t*>(c.take(1, 4));
+  const int ks = router_slices(T, E, H);
+  m.rparts = ks > 1 ? static_cast<float*>(c.take(int64_t(ks) * T * E, 4)) : nullptr;
   // the grouped GEMM addresses these with 32-bit offsets
   if (m.act_bytes > size_t(INT32_MAX) || m.xs_bytes > size_t(INT32_MAX)) c.overflow = true;
   if (out) *out = m;
@@ -394,15 +397,26 @@ dsq_status run_moe(const float* X, const float* gamma, float eps, float* xn, con
     return DSQ_OK;
   }
   if (!given) {
-    // (0) + (1) normalisation and router logits, fp32, bias included
-    if (T <= 32) {
+    // (0) + (1) normalisation and router logits, fp32, bias included;
+    // (2) softmax + top-k + renormalisation.  Up to 32 tokens the GEMV router
+    // (the norm fused in) serves the block and shapes the matrix-core router
+    // does not take; otherwise the matrix-core router, its K split over
+    // several workgroups when the token x expert tiles are too few to fill
+    // the chip, the slices added by the top-k kernel.
+    const int ks = router_slices(T, E, H);
+    if (T <= 32 && (gamma || ks == 0)) {
       DSQ_TRY(launch_router_gemv(X, T, router_w, bias, E, H, m.logits, gamma, eps, xn, st));
+      DSQ_TRY(launch_topk(m.logits, nullptr, T, E, top_k, m.idx, m.w, st));
     } else {
       if (gamma) DSQ_TRY(launch_rmsnorm(X, gamma, T, H, eps, xn, st));
-      DSQ_TRY(launch_router(Xe, T, router_w, bias, E, H, m.logits, st));
+      if (ks > 1) {
+        DSQ_TRY(launch_router(Xe, T, router_w, nullptr, E, H, m.rparts, ks, st));
+        DSQ_TRY(launch_topk_parts(m.rparts, ks, bias, m.logits, T, E, top_k, m.idx, m.w, st));
+      } else {
+        DSQ_TRY(launch_router(Xe, T, router_w, bias, E, H, m.logits, ks, st));
+        DSQ_TRY(launch_topk(m.logits, nullptr, T, E, top_k, m.idx, m.w, st));
+      }
     }
-    // (2) softmax + top-k + renormalisation
-    DSQ_TRY(launch_topk(m.logits, nullptr, T, E, top_k, m.idx, m.w, st));
   }
   // (3) stable grouping by expert, and the token tiles of the grouped GEMMs
   const int xp = bf16 ? 1 : 2;
@@ -651,7 +665,8 @@ dsq_status dsq_moe_ffn_cached(const float* X, const float* router_w, const float
   if (T <= 32) {
     DSQ_TRY(launch_router_gemv(X, T, router_w, bias, E, H, logits, nullptr, 0.0f, nullptr, st));
   } else {
-    DSQ_TRY(launch_router(X, T, router_w, bias, E, H, logits, st));
+    DSQ_TRY(launch_router(X, T, router_w, bias, E, H, logits,
+                          router_slices(T, E, H) > 0 ? 1 : 0, st));
   }
   DSQ_TRY(launch_topk(logits, nullptr, T, E, top_k, idx, w, st));
   // (2) the host sees the routing

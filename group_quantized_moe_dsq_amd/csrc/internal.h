@@ -39,12 +39,22 @@ struct Groups {
 //  dense -> X + m*K ; moe gather -> X + (perm[p]/top_k)*K ; moe segment -> X + p*K.
 enum XRows { XR_DENSE = 0, XR_GATHER = 1, XR_SEGMENT = 2 };
 
-// fp32 router: logits[t][e] = X[t] . Wr[e] (+ bias[e])
+// fp32 router: logits[t][e] = X[t] . Wr[e] (+ bias[e]), on the matrix cores with K split over ks workgroups
+// (ks = router_slices(T, E, H); 0 = the VALU kernel).  ks == 1: logits
+// [T][E] with the bias; ks > 1: partial sums [ks][T][E] without it, for
+// launch_topk_parts.
+constexpr int kRouterMaxSlices = 16;
+int router_slices(int64_t T, int32_t E, int64_t H);
 hipError_t launch_router(const float* X, int64_t T, const float* Wr, const float* bias,
-                         int32_t E, int64_t H, float* logits, hipStream_t stream);
+                         int32_t E, int64_t H, float* logits, int ks, hipStream_t stream);
 
 hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
                        int32_t* idx, float* w, hipStream_t stream);
+// top-k on the router's K slices: logits = sum of the slices in order + rbias
+// (written out), then as launch_topk without a selection bias
+hipError_t launch_topk_parts(const float* parts, int nparts, const float* rbias, float* logits,
+                             int64_t T, int32_t E, int32_t k, int32_t* idx, float* w,
+                             hipStream_t stream);
 
 // Stable grouping of the T*k routing entries by expert (one workgroup).
 // With tiles, also the token-tile table of the grouped GEMM for tiles of tpt

@@ -25,8 +25,9 @@ struct RouterArgs {
   int N, K;         // N = E
   const float* X;   // [M][K]
   int64_t M;
-  float* out;       // [M][N]
+  float* out;       // [M][N]; with ks > 1: [ks][M][N] partial sums, no bias
   const float* bias;
+  int ks;           // K slices (grid y)
 };
 
 constexpr int kRound = 1024;  // K per LDS round: 64 lanes x 16
@@ -132,7 +133,9 @@ __global__ __launch_bounds__(256) void router_kernel(RouterArgs p) {
 // bytes per instruction.  Lane l supplies
 // A[token l%16] and B[expert l%16]; its 4 results are tokens 4(l/16) .. +3 of
 // expert l%16.  The waves' partial tiles meet in LDS in a fixed order.
-// Requires K % (256 NW) == 0 (whole stages of 64 k per wave, four stages).
+// Requires K % (256 NW) == 0.  With few tiles, K is also split over ks
+// workgroups (grid y, slice s takes K range s of ks); each writes its partial
+// tile, and the top-k kernel adds the slices in order and the bias.
 // ---------------------------------------------------------------------------
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
@@ -163,20 +166,23 @@ __global__ __launch_bounds__(64 * kRouterNW) void router_mfma_kernel(RouterArgs 
   }
   const int e0 = te * 16;
   const int64_t t0 = int64_t(tt) * 16;
-  const int K = p.K, KQ = K / kRouterNW;  // K range per wave
+  const int K = p.K, KQ = K / (kRouterNW * p.ks);  // K range per wave
+  const int k0 = blockIdx.y * (K / p.ks) + wv * KQ;
   const int64_t tr = t0 + r16 < p.M ? t0 + r16 : p.M - 1;  // clamped rows: loads stay in range
   const int er = e0 + r16 < p.N ? e0 + r16 : p.N - 1;
   // lane group g holds elements 4g .. 4g+3 of every 16-element chunk of the
   // wave's K range: the four groups of a row read one contiguous 64 bytes
-  const float4* xa = reinterpret_cast<const float4*>(p.X + tr * K + wv * KQ) + g;
-  const float4* wb = reinterpret_cast<const float4*>(p.W + int64_t(er) * K + wv * KQ) + g;
+  const float4* xa = reinterpret_cast<const float4*>(p.X + tr * K + k0) + g;
+  const float4* wb = reinterpret_cast<const float4*>(p.W + int64_t(er) * K + k0) + g;
   f32x4v acc = {0.f, 0.f, 0.f, 0.f};
   // chunks of 4 float4 per operand (16 MFMAs); four register stages, loads
   // three chunks ahead.  Chunk indices past the end are clamped, so every
-  // load is unconditional and the compiler's waits stay static.
-  const int nch = KQ / 64;  // stages of 4 chunks; a multiple of 4 (K % (256 NW) == 0)
+  // load is unconditional and the compiler's waits stay static; the
+  // multiply-adds of chunks past the end are skipped (uniform branches).
+  const int nch = KQ / 64;  // chunks of 64 k (>= 1: K % (64 NW ks) == 0)
   float4 a[4][4], b[4][4];
   auto load = [&](float4 (&av)[4], float4 (&bv)[4], int c) {
+    if (nch < 4 && c >= nch) return;  // short ranges: no loads past the end
     const int cc = c < nch ? c : nch - 1;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -205,15 +211,15 @@ __global__ __launch_bounds__(64 * kRouterNW) void router_mfma_kernel(RouterArgs 
     __builtin_amdgcn_sched_barrier(0);
     load(a[0], b[0], c + 4);
     __builtin_amdgcn_sched_barrier(0);
-    mma(a[1], b[1]);
+    if (c + 1 < nch) mma(a[1], b[1]);
     __builtin_amdgcn_sched_barrier(0);
     load(a[1], b[1], c + 5);
     __builtin_amdgcn_sched_barrier(0);
-    mma(a[2], b[2]);
+    if (c + 2 < nch) mma(a[2], b[2]);
     __builtin_amdgcn_sched_barrier(0);
     load(a[2], b[2], c + 6);
     __builtin_amdgcn_sched_barrier(0);
-    mma(a[3], b[3]);
+    if (c + 3 < nch) mma(a[3], b[3]);
     __builtin_amdgcn_sched_barrier(0);
   }
   part[wv][lane] = acc;
@@ -224,11 +230,13 @@ __global__ __launch_bounds__(64 * kRouterNW) void router_mfma_kernel(RouterArgs 
     for (int w = 1; w < kRouterNW; ++w) v += part[w][lane];
     const int e = e0 + r16;
     if (e < p.N) {
-      const float b = p.bias ? p.bias[e] : 0.0f;
+      const bool add_bias = p.bias && p.ks == 1;
+      const float b = add_bias ? p.bias[e] : 0.0f;
+      float* out = p.out + int64_t(blockIdx.y) * p.M * p.N;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int64_t t = t0 + 4 * g + q;
-        if (t < p.M) p.out[t * p.N + e] = p.bias ? v[q] + b : v[q];
+        if (t < p.M) out[t * p.N + e] = add_bias ? v[q] + b : v[q];
       }
     }
   }
@@ -241,9 +249,19 @@ __global__ __launch_bounds__(64 * kRouterNW) void router_mfma_kernel(RouterArgs 
 #define DSQ_ROUTER_MT 8  // tokens per tile
 #endif
 
+int router_slices(int64_t T, int32_t E, int64_t H) {
+  const int64_t tiles = ((E + 15) / 16) * ((T + 15) / 16);
+  if (H % (256 * kRouterNW) != 0 || tiles > int64_t(INT32_MAX)) return 0;
+  int ks = 1;
+  while (2 * ks <= kRouterMaxSlices && tiles * 2 * ks <= 256 && H % (64 * kRouterNW * 2 * ks) == 0)
+    ks *= 2;
+  return ks;
+}
+
 hipError_t launch_router(const float* X, int64_t T, const float* Wr, const float* bias,
-                         int32_t E, int64_t H, float* logits, hipStream_t stream) {
-  if (H % (256 * kRouterNW) == 0 && ((E + 15) / 16) * ((T + 15) / 16) <= int64_t(INT32_MAX)) {
+                         int32_t E, int64_t H, float* logits, int ks, hipStream_t stream) {
+  if (ks >= 1) {
+    if (ks > router_slices(T, E, H)) return hipErrorInvalidValue;
     RouterArgs a{};
     a.W = Wr;
     a.N = E;
@@ -252,8 +270,10 @@ hipError_t launch_router(const float* X, int64_t T, const float* Wr, const float
     a.M = T;
     a.out = logits;
     a.bias = bias;
+    a.ks = ks;
     if (T == 0 || E == 0) return hipSuccess;
-    hipLaunchKernelGGL(router_mfma_kernel, dim3(unsigned(((E + 15) / 16) * ((T + 15) / 16))),
+    hipLaunchKernelGGL(router_mfma_kernel, dim3(unsigned(((E + 15) / 16) * ((T + 15) / 16)),
+                                                unsigned(ks)),
                        dim3(64 * kRouterNW), 0, stream, a);
     return hipGetLastError();
   }
@@ -282,9 +302,14 @@ hipError_t launch_router(const float* X, int64_t T, const float* Wr, const float
 // (score desc, index desc); lane i keeps the i-th winner.  The renormalised
 // weight of a selected expert is exp(s_i - s_max) / sum_sel exp(s_j - s_max):
 // the full softmax denominator cancels in p_i / sum_sel p_j.
+// With nparts > 1 the input is the router's K slices [nparts][T][E]: they are
+// added in slice order, then the router bias rbias, and the sums are written
+// to lout (the layer's logits) before the selection.
 // ---------------------------------------------------------------------------
 template <int EPL>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits,
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int nparts,
+                                                   const float* __restrict__ rbias,
+                                                   float* __restrict__ lout,
                                                    const float* __restrict__ bias, int T, int E,
                                                    int k, int32_t* __restrict__ idx,
                                                    float* __restrict__ wout) {
@@ -296,6 +321,36 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   // all loads first (clamped addresses, no branches), then the fix-ups
 #pragma unroll
   for (int j = 0; j < EPL; ++j) v[j] = logits[int64_t(t) * E + min(lane + 64 * j, E - 1)];
+  if (nparts > 1) {
+    // every slice's and the bias's loads in flight before the first add (up
+    // to eight slices; more take further rounds); slices added in order
+    const int64_t ps = int64_t(T) * E;
+    float u[7][EPL], rb[EPL];
+#pragma unroll
+    for (int q = 0; q < 7; ++q)
+#pragma unroll
+      for (int j = 0; j < EPL; ++j)
+        u[q][j] = logits[min(1 + q, nparts - 1) * ps + int64_t(t) * E + min(lane + 64 * j, E - 1)];
+#pragma unroll
+    for (int j = 0; j < EPL; ++j) rb[j] = rbias ? rbias[min(lane + 64 * j, E - 1)] : 0.0f;
+#pragma unroll
+    for (int q = 0; q < 7; ++q) {
+      if (1 + q >= nparts) break;
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) v[j] += u[q][j];
+    }
+    for (int q = 8; q < nparts; ++q) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) v[j] += logits[q * ps + int64_t(t) * E + min(lane + 64 * j, E - 1)];
+    }
+    if (rbias) {
+#pragma unroll
+      for (int j = 0; j < EPL; ++j) v[j] += rb[j];
+    }
+#pragma unroll
+    for (int j = 0; j < EPL; ++j)
+      if (lane + 64 * j < E) lout[int64_t(t) * E + lane + 64 * j] = v[j];
+  }
   if (bias) {
     float b[EPL];
 #pragma unroll
@@ -339,14 +394,17 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   }
 }
 
-hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
-                       int32_t* idx, float* w, hipStream_t stream) {
+namespace {
+
+hipError_t topk_any(const float* logits, int nparts, const float* rbias, float* lout,
+                    const float* bias, int64_t T, int32_t E, int32_t k, int32_t* idx, float* w,
+                    hipStream_t stream) {
   if (T == 0) return hipSuccess;
   const int64_t blocks = (T + 3) / 4;
   const int epl = (E + 63) / 64;
-#define DSQ_TOPK(n)                                                                        \
-  hipLaunchKernelGGL(topk_kernel<n>, dim3(unsigned(blocks)), dim3(256), 0, stream, logits, \
-                     bias, int(T), E, k, idx, w)
+#define DSQ_TOPK(n)                                                                          \
+  hipLaunchKernelGGL(topk_kernel<n>, dim3(unsigned(blocks)), dim3(256), 0, stream, logits,   \
+                     nparts, rbias, lout, bias, int(T), E, k, idx, w)
   if (epl <= 1) DSQ_TOPK(1);
   else if (epl <= 2) DSQ_TOPK(2);
   else if (epl <= 4) DSQ_TOPK(4);
@@ -356,6 +414,20 @@ hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int32_
   else DSQ_TOPK(64);
 #undef DSQ_TOPK
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
+                       int32_t* idx, float* w, hipStream_t stream) {
+  return topk_any(logits, 1, nullptr, nullptr, bias, T, E, k, idx, w, stream);
+}
+
+hipError_t launch_topk_parts(const float* parts, int nparts, const float* rbias, float* logits,
+                             int64_t T, int32_t E, int32_t k, int32_t* idx, float* w,
+                             hipStream_t stream) {
+  if (nparts < 2 || !logits) return hipErrorInvalidValue;
+  return topk_any(parts, nparts, rbias, logits, nullptr, T, E, k, idx, w, stream);
 }
 
 // ---------------------------------------------------------------------------

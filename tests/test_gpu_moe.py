@@ -57,7 +57,10 @@ SMALL = [(8, 256, 128, 4, 64, 2, 1), (8, 256, 128, 4, 64, 2, 5), (16, 128, 192, 
          (8, 256, 128, 4, 64, 2, 3), (16, 512, 256, 8, 128, 6, 4), (4, 8192, 128, 8, 64, 2, 2),
          (4, 384, 128, 8, 128, 1, 17), (32, 512, 256, 4, 128, 6, 40),
          # ~20 tokens per expert: three token tiles of one expert in flight
-         (4, 256, 128, 8, 64, 2, 40)]
+         (4, 256, 128, 8, 64, 2, 40),
+         # H a multiple of 1024: the matrix-core router with K split in 4 / 8
+         # slices added by the top-k kernel (ragged token and expert tiles)
+         (16, 1024, 128, 4, 64, 2, 9), (24, 2048, 128, 8, 128, 3, 40)]
 
 
 @pytest.mark.parametrize("E,H,I,bits,group,k,T", SMALL)
@@ -70,7 +73,8 @@ def test_moe_fp32_small(E, H, I, bits, group, k, T):
 
 @pytest.mark.parametrize("E,H,I,bits,group,k,T", [(8, 256, 128, 8, 128, 2, 64),
                                                   (16, 512, 256, 4, 64, 4, 100),
-                                                  (8, 128, 192, 8, 64, 3, 7)])
+                                                  (8, 128, 192, 8, 64, 3, 7),
+                                                  (16, 1024, 256, 4, 64, 4, 100)])
 def test_moe_bf16_small(E, H, I, bits, group, k, T):
     say(f"moe bf16 E={E} H={H} I={I} bits={bits} group={group} k={k} T={T}")
     fx = MoeFixture(E, H, I, bits, group, seed=5)

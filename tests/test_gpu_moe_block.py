@@ -74,7 +74,9 @@ def check_block(fx: MoeFixture, X, g, k, math, rel, tokens=None):
 # kernels, norm fused into the router; > 32: separate norm kernel
 CASES = [(8, 256, 128, 4, 64, 2, 1, dsq.MATH_FP32), (16, 512, 256, 8, 128, 6, 4, dsq.MATH_FP32),
          (8, 256, 128, 4, 64, 2, 5, dsq.MATH_FP32), (16, 128, 192, 8, 64, 4, 33, dsq.MATH_FP32),
-         (8, 256, 128, 8, 128, 2, 64, dsq.MATH_BF16_MFMA), (4, 8192, 128, 8, 64, 2, 2, dsq.MATH_FP32)]
+         (8, 256, 128, 8, 128, 2, 64, dsq.MATH_BF16_MFMA), (4, 8192, 128, 8, 64, 2, 2, dsq.MATH_FP32),
+         # norm kernel, then the matrix-core router with K in 8 slices
+         (24, 2048, 128, 4, 64, 2, 40, dsq.MATH_FP32)]
 
 
 @pytest.mark.parametrize("E,H,I,bits,group,k,T,math", CASES)
