@@ -506,20 +506,20 @@ hipError_t launch_one(const GmmArgs& a, int64_t max_tiles, hipStream_t stream) {
 }
 
 template <int XP>
-hipError_t launch_bits(const GmmArgs& a, int bits, bool swiglu, int64_t max_items,
+hipError_t launch_bits(const GmmArgs& a, int bits, bool swiglu, int64_t max_tiles,
                        hipStream_t stream) {
   const int J = a.group / 32;
   if (bits == 4 && J == 2)
-    return swiglu ? launch_one<4, 2, XP, true>(a, max_items, stream)
-                  : launch_one<4, 2, XP, false>(a, max_items, stream);
+    return swiglu ? launch_one<4, 2, XP, true>(a, max_tiles, stream)
+                  : launch_one<4, 2, XP, false>(a, max_tiles, stream);
   if (bits == 4 && J == 4)
-    return swiglu ? launch_one<4, 4, XP, true>(a, max_items, stream)
-                  : launch_one<4, 4, XP, false>(a, max_items, stream);
+    return swiglu ? launch_one<4, 4, XP, true>(a, max_tiles, stream)
+                  : launch_one<4, 4, XP, false>(a, max_tiles, stream);
   if (bits == 8 && J == 2)
-    return swiglu ? launch_one<8, 2, XP, true>(a, max_items, stream)
-                  : launch_one<8, 2, XP, false>(a, max_items, stream);
-  return swiglu ? launch_one<8, 4, XP, true>(a, max_items, stream)
-                : launch_one<8, 4, XP, false>(a, max_items, stream);
+    return swiglu ? launch_one<8, 2, XP, true>(a, max_tiles, stream)
+                  : launch_one<8, 2, XP, false>(a, max_tiles, stream);
+  return swiglu ? launch_one<8, 4, XP, true>(a, max_tiles, stream)
+                : launch_one<8, 4, XP, false>(a, max_tiles, stream);
 }
 
 }  // namespace

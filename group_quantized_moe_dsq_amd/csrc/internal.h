@@ -26,7 +26,7 @@ struct Groups {
   const int32_t* offsets;   // [E+1] segment starts in perm order
   const int32_t* perm;      // [T*k] entry j = t*k+i in (expert, j) order
   int32_t top_k;
-  int32_t max_items;        // grid bound on the number of active experts
+  int32_t max_items;        // bound on the number of active experts (0: no rows)
   // token tiles in (active expert, tile) order, one record each:
   // {expert, first row in perm order, rows in the tile (<= 16 / xp),
   //  activation tile index}; count in *n_tiles, at most max_tiles
