@@ -91,3 +91,11 @@ def test_cached_moe_decode_full_size():
     say("cached moe decode full size")
     fx = MoeFixture(256, 4096, 2048, 4, 64, seed=0)
     run_stream(fx, 6, 16, [1, 1, 1, 1], seed=11)
+
+
+def test_cached_moe_many_tokens_matrix_core_router():
+    """Calls of 40 and 36 tokens: the routing runs on the matrix-core router
+    (H a multiple of 1024), all 16 experts fit the 16 slots."""
+    say("cached moe many tokens")
+    fx = MoeFixture(16, 1024, 128, 4, 64, seed=12, bias_std=0.5)
+    run_stream(fx, 2, 16, [40, 36], seed=12)
