@@ -20,7 +20,7 @@
 // k are the answer (the top k of all values lie among every chunk's top k).
 // For small k a workgroup takes the block maximum of a 4096-key chunk k times
 // (the pick is removed by the one lane that holds it); for larger k it sorts
-// a 1024-key chunk in LDS with a bitonic network.
+// a 1024-key chunk with a bitonic network held in registers.
 #include "common.h"
 #include "internal.h"
 #include "mfma_util.h"
@@ -92,9 +92,27 @@ __device__ __forceinline__ void head_emit(uint64_t key, int r, const float* __re
   }
 }
 
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const int lo = __shfl_xor(int(uint32_t(v)), m), hi = __shfl_xor(int(uint32_t(v >> 32)), m);
+  return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+}
+
 // One round, bitonic path.  FROM_Y: the input is the logits (keys are formed
 // here), else the previous round's keys.  FINAL (one workgroup): write the k
 // best as (index, value); else write them as keys to out[block][k].
+//
+// The chunk's 1024 keys stay in registers, thread t holding positions 2t and
+// 2t + 1 (a wave owns 128 consecutive positions).  Every step of the network
+// (blocks of `size` sorted in alternating direction, the last one descending)
+// pairs position p with p ^ stride: stride 1 is inside a thread, strides 2 ..
+// 64 pair lanes of one wave (a lane exchange), and only strides 128 .. 512
+// (6 of the 55 steps) go through LDS, each with one barrier (two LDS buffers
+// alternate, so a step's writes never meet the previous step's reads).  Both
+// members of a pair compute their new key from the same two keys: the lower
+// position keeps the larger one in a descending block, the smaller one in an
+// ascending block.
 template <bool FROM_Y, bool FINAL>
 __global__ __launch_bounds__(kHeadSortThreads) void head_round_kernel(const float* __restrict__ y,
                                                                       const uint64_t* __restrict__ in,
@@ -102,35 +120,50 @@ __global__ __launch_bounds__(kHeadSortThreads) void head_round_kernel(const floa
                                                                       uint64_t* __restrict__ out,
                                                                       int32_t* __restrict__ idx,
                                                                       float* __restrict__ val) {
-  __shared__ uint64_t s[kHeadChunk];
+  __shared__ uint64_t s[2][kHeadChunk];
+  const int t = threadIdx.x;
   const int64_t base = int64_t(blockIdx.x) * kHeadChunk;
+  uint64_t v[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int j = threadIdx.x + h * kHeadSortThreads;
-    const int64_t i = base + j;
+  for (int b = 0; b < 2; ++b) {
+    const int64_t i = base + 2 * t + b;
     uint64_t key = 0;
     if (i < n) key = FROM_Y ? head_key(y[i], uint32_t(i)) : in[i];
-    s[j] = key;
+    v[b] = key;
   }
-  lds_barrier();
-  // bitonic network: blocks of `size` alternate direction, the last one
-  // (size = 1024) sorts the chunk descending; thread t owns the pair
-  // (lo, lo + stride) of every step.  (Steps of stride <= 64 stay inside a
-  // wave's own 128 keys and could skip the barrier, but measured slower.)
-  const int t = threadIdx.x;
+  int buf = 0;
+#pragma unroll
   for (int size = 2; size <= kHeadChunk; size <<= 1) {
+#pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const int lo = 2 * t - (t & (stride - 1));
-      const bool desc = (lo & size) == 0;
-      const uint64_t a = s[lo], b = s[lo + stride];
-      if ((a < b) == desc) {
-        s[lo] = b;
-        s[lo + stride] = a;
+      uint64_t o[2];
+      if (stride == 1) {
+        o[0] = v[1];
+        o[1] = v[0];
+      } else if (stride <= 64) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) o[b] = shfl_xor64(v[b], stride >> 1);
+      } else {
+        s[buf][2 * t] = v[0];
+        s[buf][2 * t + 1] = v[1];
+        lds_barrier();
+#pragma unroll
+        for (int b = 0; b < 2; ++b) o[b] = s[buf][(2 * t + b) ^ stride];
+        buf ^= 1;
       }
-      lds_barrier();
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int pos = 2 * t + b;
+        const bool lower = (pos & stride) == 0, desc = (pos & size) == 0;
+        v[b] = lower == desc ? umax64(v[b], o[b]) : umin64(v[b], o[b]);
+      }
     }
   }
-  for (int r = t; r < k; r += kHeadSortThreads) head_emit<FINAL>(s[r], r, y, out, idx, val, k);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int r = 2 * t + b;
+    if (r < k) head_emit<FINAL>(v[b], r, y, out, idx, val, k);
+  }
 }
 
 // One round, pick path: k times the block maximum of the workgroup's chunk.
