@@ -32,7 +32,7 @@ constexpr int kHeadSortThreads = kHeadChunk / 2;  // one pair per thread and ste
 constexpr int kHeadThreads = 256;     // pick path
 constexpr int kHeadWaves = kHeadThreads / 64;
 #ifndef DSQ_HEAD_PICK_MAXK
-#define DSQ_HEAD_PICK_MAXK 16
+#define DSQ_HEAD_PICK_MAXK 6  // picks cost ~1.1 us each; the sort path ~13.5 us up to k = 8
 #endif
 constexpr int kHeadPickMaxK = DSQ_HEAD_PICK_MAXK;
 constexpr int kHeadPickPer = 16;      // keys per thread, pick path

@@ -39,7 +39,9 @@ def values(N, pattern, seed):
 
 CASES = [(1, 1, "normal"), (5, 5, "ties"), (1023, 64, "normal"), (1024, 1, "special"),
          (1025, 256, "ties"), (2049, 17, "special"), (70000, 50, "normal"),
-         (70000, 256, "ties"), (129280, 1, "special"), (300001, 100, "special")]
+         (70000, 256, "ties"), (129280, 1, "special"), (300001, 100, "special"),
+         # either side of the pick / sort switch (k <= 6 picks)
+         (129280, 6, "special"), (129280, 7, "ties"), (5000, 8, "special")]
 
 
 @pytest.mark.parametrize("N,k,pattern", CASES)
