@@ -42,7 +42,7 @@ def qbytes(bits, group, K, N):
 
 
 # the sources that define the dominant kernel (the fused-dequant GEMV)
-GEMV_SOURCES = ("gemv.hip", "gemv_core.h", "common.h")
+GEMV_SOURCES = ("gemv.hip", "gemv_core.h", "head_key.h", "common.h")
 
 
 def kernel_source_hash():

@@ -302,6 +302,14 @@ dsq_status dsq_gemv_topk(const dsq_qweight* W, int64_t expert, const float* x, f
   if (!aligned(workspace, 256)) return DSQ_ERR_ALIGN;
   if ((s = check_device()) != DSQ_OK) return s;
   hipStream_t st = (hipStream_t)stream;
+  if (k == 1 && gemv_argmax_supported(*W)) {
+    // top-1: the GEMV's waves rank their own outputs; one pick over their keys
+    uint64_t* keys = static_cast<uint64_t*>(workspace);
+    int64_t n = 0;
+    hipError_t e = launch_gemv_argmax(*W, expert, x, y, keys, &n, st);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(launch_head_from_keys(y, keys, n, idx, values, st));
+  }
   hipError_t e = launch_gemv(*W, expert, x, y, st);
   if (e != hipSuccess) return hip_status(e);
   return hip_status(launch_head(y, W->N, k, idx, values, workspace, st));

@@ -21,6 +21,7 @@
 //     step's loads are issued before the current step's arithmetic.
 #include "common.h"
 #include "gemv_core.h"
+#include "head_key.h"
 #include "internal.h"
 
 namespace dsq {
@@ -99,6 +100,72 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ p
   }
 }
 
+// The same loop as gemv_kernel, plus every wave's best rank key (head_key.h)
+// of the rows it stored, written to wkey[wave]: the output head's top-1
+// without a separate pass over the logits.  (A separate kernel, so that
+// gemv_kernel's code stays as tuned.)
+template <int BITS, int R, int KCH>
+__global__ __launch_bounds__(256) void gemv_argmax_kernel(const uint8_t* __restrict__ payload,
+                                                          const float2* __restrict__ meta,
+                                                          const float* __restrict__ x,
+                                                          float* __restrict__ y, int N, int K,
+                                                          int group, uint64_t* __restrict__ wkey) {
+  const int lane = threadIdx.x & 63;
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int nwaves = (gridDim.x * blockDim.x) >> 6;
+  const int row_bytes = K * BITS / 8;
+  const int nchunk = row_bytes / 16;
+  const int groups = K / group;
+
+  auto load = [&](RowChunks<BITS, R, KCH>& C, int rb) {
+    const uint8_t* prow[R];
+    const float2* mrow[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = min(rb * R + r, N - 1);
+      prow[r] = payload + int64_t(row) * row_bytes;
+      mrow[r] = meta + int64_t(row) * groups;
+    }
+    C.load(prow, mrow, nchunk, group, lane);
+  };
+  XSlice<BITS, KCH> xs;
+  uint64_t best = 0;  // the best key of the rows this lane stored
+  auto finish = [&](const RowChunks<BITS, R, KCH>& C, int rb) {
+    float acc[R];
+    C.dot(xs, acc);
+    const float tot = wave_reduce_scatter<R>(acc);
+    if ((lane & (64 / R - 1)) == 0) {
+      const int row = rb * R + reduce_scatter_row<R>(lane);
+      if (row < N) {
+        y[row] = tot;
+        best = umax64(best, head_key(tot, uint32_t(row)));
+      }
+    }
+  };
+
+  extern __shared__ float4 xl[];
+  RowChunks<BITS, R, KCH> A, B;
+  int rb = wave;
+  if (rb * R < N) load(A, rb);
+  stage_lds<Codes<BITS>::kPerChunk / 4>(x, K, xl);
+  __syncthreads();
+  xs.load_lds(xl, nchunk, lane);
+  xs.sums();
+  while (rb * R < N) {
+    const int rb1 = rb + nwaves;
+    const bool more1 = rb1 * R < N;
+    if (more1) load(B, rb1);
+    finish(A, rb);
+    if (!more1) break;
+    const int rb2 = rb1 + nwaves;
+    if (rb2 * R < N) load(A, rb2);
+    finish(B, rb1);
+    rb = rb2;
+  }
+  const uint64_t b = wave_max_key(best);  // every lane active: the loop is wave-uniform
+  if (lane == 0) wkey[wave] = b;
+}
+
 // Rows longer than KMAX chunks per lane: x is re-read from memory (L1/L2)
 // for every chunk instead of being held in registers.
 template <int BITS, int R>
@@ -166,12 +233,18 @@ int max_waves(int rowblocks) {
 
 template <int BITS, int R, int KCH>
 hipError_t go(const QMat& q, const float* x, float* y, int N, int K, int group,
-              hipStream_t stream) {
+              uint64_t* wkey, int64_t* nkeys, hipStream_t stream) {
   const int rowblocks = (N + R - 1) / R;
   const int waves = rowblocks < max_waves(rowblocks) ? rowblocks : max_waves(rowblocks);
   const int blocks = (waves + 3) / 4;
-  hipLaunchKernelGGL((gemv_kernel<BITS, R, KCH>), dim3(blocks), dim3(256), size_t(K) * 4, stream,
-                     q.payload, q.meta, x, y, N, K, group);
+  if (wkey) {
+    hipLaunchKernelGGL((gemv_argmax_kernel<BITS, R, KCH>), dim3(blocks), dim3(256),
+                       size_t(K) * 4, stream, q.payload, q.meta, x, y, N, K, group, wkey);
+    *nkeys = int64_t(blocks) * 4;
+  } else {
+    hipLaunchKernelGGL((gemv_kernel<BITS, R, KCH>), dim3(blocks), dim3(256), size_t(K) * 4,
+                       stream, q.payload, q.meta, x, y, N, K, group);
+  }
   return hipGetLastError();
 }
 
@@ -186,18 +259,22 @@ hipError_t go_long(const QMat& q, const float* x, float* y, int N, int K, int gr
   return hipGetLastError();
 }
 
+// wkey: also write every wave's best key there (rows of at most 4 chunks per
+// lane only; the caller checks gemv_argmax_supported) and their count to nkeys
 template <int BITS>
 hipError_t dispatch(const QMat& q, const float* x, float* y, int N, int K, int group,
-                    hipStream_t stream) {
+                    uint64_t* wkey, int64_t* nkeys, hipStream_t stream) {
   const int nchunk = K * BITS / 8 / 16;
   const int kch = (nchunk + 63) / 64;
   constexpr int R = BITS == 8 ? DSQ_GEMV_R8 : DSQ_GEMV_R4;
   switch (kch) {
-    case 1: return go<BITS, R, 1>(q, x, y, N, K, group, stream);
-    case 2: return go<BITS, R, 2>(q, x, y, N, K, group, stream);
-    case 3: return go<BITS, R, 3>(q, x, y, N, K, group, stream);
-    case 4: return go<BITS, R, 4>(q, x, y, N, K, group, stream);
-    default: return go_long<BITS, 4>(q, x, y, N, K, group, stream);
+    case 1: return go<BITS, R, 1>(q, x, y, N, K, group, wkey, nkeys, stream);
+    case 2: return go<BITS, R, 2>(q, x, y, N, K, group, wkey, nkeys, stream);
+    case 3: return go<BITS, R, 3>(q, x, y, N, K, group, wkey, nkeys, stream);
+    case 4: return go<BITS, R, 4>(q, x, y, N, K, group, wkey, nkeys, stream);
+    default:
+      if (wkey) return hipErrorNotSupported;
+      return go_long<BITS, 4>(q, x, y, N, K, group, stream);
   }
 }
 
@@ -208,8 +285,28 @@ hipError_t launch_gemv(const dsq_qweight& W, int64_t expert, const float* x, flo
   if (W.group == kSuperGroup) return launch_gemv_sb4(W, expert, x, y, stream);
   const QMat q = entry(W, expert);
   const int N = int(W.N), K = int(W.K);
-  if (W.bits == 8) return dispatch<8>(q, x, y, N, K, W.group, stream);
-  return dispatch<4>(q, x, y, N, K, W.group, stream);
+  if (W.bits == 8) return dispatch<8>(q, x, y, N, K, W.group, nullptr, nullptr, stream);
+  return dispatch<4>(q, x, y, N, K, W.group, nullptr, nullptr, stream);
+}
+
+bool gemv_argmax_supported(const dsq_qweight& W) {
+  return W.group != kSuperGroup && (W.K * W.bits / 8 / 16 + 63) / 64 <= 4;
+}
+
+size_t gemv_argmax_key_bytes() {
+  const int most = 256 * (DSQ_GEMV_WAVES_PER_CU > DSQ_GEMV_WAVES_PER_CU_LARGE
+                              ? DSQ_GEMV_WAVES_PER_CU
+                              : DSQ_GEMV_WAVES_PER_CU_LARGE);
+  return size_t(align256(int64_t(most + 3) * 8));
+}
+
+hipError_t launch_gemv_argmax(const dsq_qweight& W, int64_t expert, const float* x, float* y,
+                              uint64_t* wkey, int64_t* nkeys, hipStream_t stream) {
+  if (!gemv_argmax_supported(W)) return hipErrorNotSupported;
+  const QMat q = entry(W, expert);
+  const int N = int(W.N), K = int(W.K);
+  if (W.bits == 8) return dispatch<8>(q, x, y, N, K, W.group, wkey, nkeys, stream);
+  return dispatch<4>(q, x, y, N, K, W.group, wkey, nkeys, stream);
 }
 
 }  // namespace dsq

@@ -23,6 +23,7 @@
 // a 1024-key chunk with a bitonic network held in registers.
 #include "common.h"
 #include "internal.h"
+#include "head_key.h"
 #include "mfma_util.h"
 
 namespace dsq {
@@ -37,45 +38,6 @@ constexpr int kHeadWaves = kHeadThreads / 64;
 constexpr int kHeadPickMaxK = DSQ_HEAD_PICK_MAXK;
 constexpr int kHeadPickPer = 16;      // keys per thread, pick path
 constexpr int kHeadPickChunk = kHeadThreads * kHeadPickPer;
-
-__device__ __forceinline__ uint64_t head_key(float v, uint32_t i) {
-  uint32_t u = __float_as_uint(v);
-  uint32_t h;
-  if (v != v) {
-    h = 0u;
-  } else {
-    if (v == 0.0f) u = 0u;  // -0 ranks with +0
-    h = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  }
-  return (uint64_t(h) << 32) | uint64_t(~i);
-}
-
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-
-// One step of a wave maximum: each lane compares with the lane the DPP
-// control names (lanes without a source, or in rows outside ROW_MASK, keep
-// their own key).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t max_step(uint64_t v) {
-  const int lo = int(uint32_t(v)), hi = int(uint32_t(v >> 32));
-  const uint32_t olo = uint32_t(__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false));
-  const uint32_t ohi = uint32_t(__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false));
-  return umax64(v, (uint64_t(ohi) << 32) | olo);
-}
-
-// The largest key of the wave, in every lane: row shifts leave each row's
-// maximum in its lane 15, the two row broadcasts carry them to lane 63.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
-  v = max_step<0x111, 0xf>(v);  // row_shr:1
-  v = max_step<0x112, 0xf>(v);  // row_shr:2
-  v = max_step<0x114, 0xf>(v);  // row_shr:4
-  v = max_step<0x118, 0xf>(v);  // row_shr:8
-  v = max_step<0x142, 0xa>(v);  // row_bcast:15
-  v = max_step<0x143, 0xc>(v);  // row_bcast:31
-  const uint32_t lo = __builtin_amdgcn_readlane(int(uint32_t(v)), 63);
-  const uint32_t hi = __builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 63);
-  return (uint64_t(hi) << 32) | lo;
-}
 
 // Write the r-th best key of a round: FINAL as (index, value), else as a key
 // of the next round's input.
@@ -239,9 +201,20 @@ void launch_round(int64_t nb, const float* y, const uint64_t* in, int64_t n, int
 }  // namespace
 
 size_t head_workspace(int64_t N, int32_t k) {
-  if (chunks(N, k) == 1) return 256;  // no intermediate keys; nonzero means supported
   // two ping-pong key buffers, each large enough for the first round's output
-  return size_t(2) * align256(chunks(N, k) * k * 8);
+  // (none when one chunk holds N: 256, nonzero means supported); for k = 1 at
+  // least the GEMV's per-wave keys
+  size_t b = chunks(N, k) == 1 ? 256 : size_t(2) * align256(chunks(N, k) * k * 8);
+  if (k == 1 && b < gemv_argmax_key_bytes()) b = gemv_argmax_key_bytes();
+  return b;
+}
+
+hipError_t launch_head_from_keys(const float* y, const uint64_t* keys, int64_t n, int32_t* idx,
+                                 float* val, hipStream_t stream) {
+  if (n < 1 || n > kHeadPickChunk || kHeadPickMaxK < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((head_pick_kernel<false, true>), dim3(1), dim3(kHeadThreads), 0, stream, y,
+                     keys, n, 1, nullptr, idx, val);
+  return hipGetLastError();
 }
 
 hipError_t launch_head(const float* y, int64_t N, int32_t k, int32_t* idx, float* val,

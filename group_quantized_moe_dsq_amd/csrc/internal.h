@@ -113,11 +113,23 @@ hipError_t launch_gmm(const dsq_qweight& A, const dsq_qweight* B, int64_t expert
                       int xp, void* act, size_t act_bytes, float* xs, size_t xs_bytes,
                       float* out, int64_t ld_out, hipStream_t stream);
 
+// GEMV that also writes every wave's best rank key (head_key.h) of its
+// outputs to wkey (at most gemv_argmax_key_bytes()) and their count to
+// nkeys; for the group formats with rows of at most 4 16-byte chunks per lane.
+bool gemv_argmax_supported(const dsq_qweight& W);
+size_t gemv_argmax_key_bytes();
+hipError_t launch_gemv_argmax(const dsq_qweight& W, int64_t expert, const float* x, float* y,
+                              uint64_t* wkey, int64_t* nkeys, hipStream_t stream);
+
 // Output-head selection: the k (<= kHeadMaxK) largest of N logits in rank
 // order (head.hip).  Workspace: head_workspace(N, k) bytes.
 constexpr int32_t kHeadMaxK = 256;
 size_t head_workspace(int64_t N, int32_t k);
 hipError_t launch_head(const float* y, int64_t N, int32_t k, int32_t* idx, float* val,
                        void* workspace, hipStream_t stream);
+// Top-1 from n (<= 4096) rank keys, e.g. launch_gemv_argmax's; y holds the
+// values the keys index.
+hipError_t launch_head_from_keys(const float* y, const uint64_t* keys, int64_t n, int32_t* idx,
+                                 float* val, hipStream_t stream);
 
 }  // namespace dsq

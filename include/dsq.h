@@ -236,7 +236,10 @@ dsq_status dsq_topk(const float* y, int64_t N, int32_t k, int32_t* idx, float* v
  * dsq_gemv_topk -- the output head: y = dequant(W[expert]) x (as dsq_gemv,
  * written to y) followed by dsq_topk(y, W->N, k, ...) on the same stream.
  * Arguments, limits and errors as the two calls; workspace:
- * dsq_topk_workspace_bytes(W->N, k).
+ * dsq_topk_workspace_bytes(W->N, k).  The result is the same as the two
+ * calls'; for k = 1 and the group formats with K * bits / 8 <= 16384 the
+ * GEMV ranks its own outputs and one small selection follows (no second
+ * pass over y).
  */
 dsq_status dsq_gemv_topk(const dsq_qweight* W, int64_t expert, const float* x, float* y,
                          int32_t k, int32_t* idx, float* values, void* workspace,

@@ -104,3 +104,38 @@ def test_gemv_topk_vocab_full_size(k):
             assert ref[0][i] - bound[i] <= lim, f"row {r} outranks the selection"
     del w, qw
     torch.cuda.empty_cache()
+
+
+# top-1 through the GEMV that ranks its own outputs: small and ragged N (waves
+# without rows write the padding key), both code widths, rows of 1..4 chunks
+# per lane, and a row length past that (the separate selection pass)
+@pytest.mark.parametrize("nbits,group,N,K", [(8, 64, 1, 256), (4, 64, 37, 512), (8, 128, 1000, 4096),
+                                            (4, 128, 5003, 8192), (8, 64, 4097, 2048),
+                                            (8, 64, 300, 12288)])
+def test_gemv_top1_matches_selection_on_its_logits(nbits, group, N, K):
+    say(f"gemv top-1 bits={nbits} group={group} N={N} K={K}")
+    w = synth.normal((N, K), 0.02, 0, synth.W, 60 + N, device="cuda")
+    # duplicated rows: equal logits, the smaller index must win
+    if N > 8:
+        w[N - 1] = w[N // 2]
+        w[3] = w[N // 2]
+    x = synth.normal((K,), 1.0, 0, synth.X, 61 + N, device="cuda")
+    qw = pack_gpu(w.contiguous(), nbits, group)
+    y, idx, val = dsq.gemv_topk(qw, x, 1)
+    y_plain = dsq.gemv(qw, x)
+    y_h = y.cpu().numpy()
+    np.testing.assert_array_equal(y_h, y_plain.cpu().numpy())
+    ref_idx, ref_val = oracle.topk(y_h, 1)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_array_equal(bits(val.cpu().numpy()), bits(ref_val))
+
+
+def test_gemv_top1_ties_take_the_smallest_index():
+    """Every row equal: all logits tie, so row 0 is the answer."""
+    say("gemv top-1 all rows equal")
+    N, K = 3000, 1024
+    row = synth.normal((1, K), 0.02, 0, synth.W, 70, device="cuda")
+    qw = pack_gpu(row.repeat(N, 1).contiguous(), 8, 64)
+    x = synth.normal((K,), 1.0, 0, synth.X, 71, device="cuda")
+    _, idx, _ = dsq.gemv_topk(qw, x, 1)
+    assert int(idx.item()) == 0
