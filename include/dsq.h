@@ -237,7 +237,7 @@ dsq_status dsq_topk(const float* y, int64_t N, int32_t k, int32_t* idx, float* v
  * written to y) followed by dsq_topk(y, W->N, k, ...) on the same stream.
  * Arguments, limits and errors as the two calls; workspace:
  * dsq_topk_workspace_bytes(W->N, k).  The result is the same as the two
- * calls'; for k = 1 and the group formats with K * bits / 8 <= 16384 the
+ * calls'; for k = 1 and the group formats with K * bits / 8 <= 4096 the
  * GEMV ranks its own outputs and one small selection follows (no second
  * pass over y).
  */
