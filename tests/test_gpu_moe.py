@@ -60,7 +60,10 @@ SMALL = [(8, 256, 128, 4, 64, 2, 1), (8, 256, 128, 4, 64, 2, 5), (16, 128, 192, 
          (4, 256, 128, 8, 64, 2, 40),
          # H a multiple of 1024: the matrix-core router with K split in 4 / 8
          # slices added by the top-k kernel (ragged token and expert tiles)
-         (16, 1024, 128, 4, 64, 2, 9), (24, 2048, 128, 8, 128, 3, 40)]
+         (16, 1024, 128, 4, 64, 2, 9), (24, 2048, 128, 8, 128, 3, 40),
+         # the largest top_k (32 of 64): decode kernels and the grouped path, and
+         # top_k = 16 through the split router
+         (64, 256, 128, 8, 64, 32, 3), (64, 256, 128, 4, 64, 32, 40), (64, 1024, 128, 8, 128, 16, 9)]
 
 
 @pytest.mark.parametrize("E,H,I,bits,group,k,T", SMALL)
