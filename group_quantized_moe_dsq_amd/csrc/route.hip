@@ -437,6 +437,9 @@ hipError_t launch_topk_parts(const float* parts, int nparts, const float* rbias,
 // selected the same expert: a bitmap [E][ceil(T/32)] with bit t of row e set
 // when token t chose e turns that into popcounts.  Integer only, so the
 // result is exact and stable (ascending token order within an expert).
+// With `tiles`, the same pass lists the grouped GEMM's token tiles: expert
+// segments cut into tiles of tpt rows, one record per tile in (active expert,
+// tile) order, written by the entry that opens the tile.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__ idx, int T, int k,
                                                      int E, uint32_t* __restrict__ bm,
