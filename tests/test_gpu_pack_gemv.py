@@ -87,7 +87,9 @@ def test_pack_flags_degenerate_and_nonfinite():
 
 GEMV_CASES = [(8, 64, 4096, 4096), (4, 64, 4096, 4096), (8, 128, 1000, 2048),
               (4, 128, 33, 384), (8, 64, 17, 64), (4, 64, 5, 8192), (8, 64, 3, 16384),
-              (4, 64, 2048, 4096), (8, 128, 4096, 2048), (4, 64, 129, 1088)]
+              (4, 64, 2048, 4096), (8, 128, 4096, 2048), (4, 64, 129, 1088),
+              # very long rows (the kernel that re-reads x per chunk)
+              (8, 64, 5, 65536), (4, 128, 3, 131072)]
 
 
 @pytest.mark.parametrize("bits,group,N,K", GEMV_CASES)
