@@ -30,6 +30,16 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 
+# Workload shape: the model constants "ds4 code walkthrough" prints (DeepSeek
+# V4 Flash architecture constants and the RMSNorm epsilon): hidden size,
+# vocabulary, routed experts, experts per token.  The expert FFN width (2048)
+# is the benchmark workload's own; the pages do not print one.
+N_EMBD = 4096
+N_VOCAB = 129280
+N_EXPERT = 256
+N_EXPERT_USED = 6
+RMS_EPS = 1e-6
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -134,8 +144,8 @@ def main():
         print(json.dumps({"calibrate_copy_bytes_read": n * 4, "bytes_written": n * 4,
                           "copies": 4}), flush=True)
         return
-    K = 4096
-    NV = 129280
+    K = N_EMBD
+    NV = N_VOCAB
 
     # ---------------- headline workload ----------------
     log("setup: INT4 g64 4096x4096 and INT8 g64 4096x129280")
@@ -265,7 +275,7 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
     torch.cuda.empty_cache()
     if "sb4vocab" in cases:
         # the vocab projection in the super-block format: 298 MB, cold by size
-        NV = 129280
+        NV = N_VOCAB
         w = synth.normal((NV, K), 0.02, 0, synth.W, 2, device=dev)
         q = dsq.QWeight(4, 256, K, NV)
         dsq.pack_weights(w, q)
@@ -284,7 +294,7 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
 
     # MoE decode layers: 256 experts, H=4096, I=2048, top-6
     def build_moe(bits, group, bias_std):
-        E, H, I = 256, 4096, 2048
+        E, H, I = N_EXPERT, N_EMBD, 2048
         router = synth.normal((E, H), 0.02, 0, synth.ROUTER, 0, device=dev)
         bias = None if bias_std is None else synth.normal((E,), bias_std, 0, synth.BIAS, 0,
                                                           device=dev)
@@ -300,18 +310,19 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
 
     def moe_case(name, layer, T, nsets, math, bits, group, iters, block=False):
         # block: the MoE step with its RMSNorm and residual (dsq_moe_block)
-        H = 4096
+        H = N_EMBD
         Xs = [synth.normal((T, H), 1.0, 0, synth.X, 1000 + T * 100 + s, device=dev)
               for s in range(nsets)]
         gamma = synth.normal((H,), 0.25, 0, synth.X, 900, device=dev) + 1.0
         wsq = dsq.moe_block_workspace_bytes if block else dsq.moe_workspace_bytes
-        ws = torch.empty(wsq(T, 256, 6, H, 2048, math) + 256, dtype=torch.uint8, device=dev)
+        ws = torch.empty(wsq(T, N_EXPERT, N_EXPERT_USED, H, 2048, math) + 256, dtype=torch.uint8,
+                         device=dev)
         Y = torch.empty((T, H), device=dev)
         counts = torch.empty(256, dtype=torch.int32, device=dev)
 
         def run(X, **kw):
             if block:
-                return dsq.moe_block(layer, X, gamma, 1e-6, math=math, Y=Y, workspace=ws, **kw)
+                return dsq.moe_block(layer, X, gamma, RMS_EPS, math=math, Y=Y, workspace=ws, **kw)
             return dsq.moe_ffn(layer, X, math=math, Y=Y, workspace=ws, **kw)
         touched = []
         for s in range(nsets):
@@ -320,8 +331,8 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
         D = float(np.mean(touched))
         ms = time_calls(lambda i: run(Xs[i % nsets]), iters, 4, torch)
         eb = 3 * qbytes(bits, group, H, 2048)
-        b = 256 * H * 4 + D * eb + 2 * T * H * 4 + (H * 4 if block else 0)
-        flops = 2 * T * 256 * H + 2 * T * 6 * 3 * H * 2048
+        b = N_EXPERT * H * 4 + D * eb + 2 * T * H * 4 + (H * 4 if block else 0)
+        flops = 2 * T * N_EXPERT * H + 2 * T * N_EXPERT_USED * 3 * H * 2048
         gbs = b / (ms * 1e-3) / 1e9
         rec = {"workload": name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "experts_touched": D,
@@ -333,17 +344,17 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
         r, b, g, u, d = build_moe(4, 64, None)
         if "moe1" in cases:
             moe_case("MoE decode T=1, 256 experts top-6, INT4 g64 SwiGLU",
-                     dsq.MoeLayer(r, g, u, d, None, 6), 1, 64, dsq.MATH_FP32, 4, 64, 64)
+                     dsq.MoeLayer(r, g, u, d, None, N_EXPERT_USED), 1, 64, dsq.MATH_FP32, 4, 64, 64)
         if "block1" in cases:
             moe_case("MoE block decode T=1 (RMSNorm + MoE + residual), INT4 g64 SwiGLU",
-                     dsq.MoeLayer(r, g, u, d, None, 6), 1, 64, dsq.MATH_FP32, 4, 64, 64,
+                     dsq.MoeLayer(r, g, u, d, None, N_EXPERT_USED), 1, 64, dsq.MATH_FP32, 4, 64, 64,
                      block=True)
         if "cache" in cases:
             expert_cache_case(dsq, synth, torch, dev, r, (g, u, d), out)
         if "moe32" in cases:
             bias = synth.normal((256,), 1.0, 0, synth.BIAS, 0, device=dev)
             moe_case("MoE batched decode T=32 skewed (router bias ~N(0,1)), INT4 g64",
-                     dsq.MoeLayer(r, g, u, d, bias, 6), 32, 8, dsq.MATH_FP32, 4, 64, 16)
+                     dsq.MoeLayer(r, g, u, d, bias, N_EXPERT_USED), 32, 8, dsq.MATH_FP32, 4, 64, 16)
         del g, u, d
         torch.cuda.empty_cache()
     if "gemm256" in cases:
@@ -351,7 +362,7 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
     if "moe256" in cases:
         r, b, g, u, d = build_moe(8, 128, None)
         moe_case("MoE prefill T=256, 256 experts top-6, INT8 g128 SwiGLU, bf16 MFMA",
-                 dsq.MoeLayer(r, g, u, d, None, 6), 256, 1, dsq.MATH_BF16_MFMA, 8, 128, 8)
+                 dsq.MoeLayer(r, g, u, d, None, N_EXPERT_USED), 256, 1, dsq.MATH_BF16_MFMA, 8, 128, 8)
         del g, u, d
         torch.cuda.empty_cache()
     return out
@@ -364,7 +375,7 @@ def expert_cache_case(dsq, synth, torch, dev, router, layer, out):
     routing of random activations is spread over all experts, so the hit
     rate follows the cache's share of them."""
     import time
-    H, I, E, k = 4096, 2048, 256, 6
+    H, I, E, k = N_EMBD, 2048, N_EXPERT, N_EXPERT_USED
     for slots in (16, 64, 256):
         c = dsq.ExpertCache(4, 64, H, I, E, slots, device=dev)
         for m, q in enumerate(layer):

@@ -542,21 +542,23 @@ dsq_status check_cache(const dsq_expert_cache* c) {
 template <class Fill>
 dsq_status cache_map(dsq_expert_cache* c, const int32_t* experts, int64_t n, int32_t* slot_out,
                      Fill&& fill) {
-  const uint64_t now = ++c->clock;
+  // every request takes the next stamp; this call's stamps are >= first
+  const uint64_t first = c->clock + 1;
   for (int64_t i = 0; i < n; ++i) {
     const int32_t e = experts[i];
     if (e < 0 || e >= c->E) return DSQ_ERR_INVALID_ARG;
+    const uint64_t now = ++c->clock;
     int32_t s = c->slot_of[e];
     if (s >= 0) {
       ++c->hits;
     } else {
-      // an empty slot (stamp 0) first, else the least recently used slot
-      // that this call has not used; ties go to the lowest index
+      // an empty slot (stamp 0; the lowest index) first, else the least
+      // recently used slot that this call has not used
       int32_t v = -1;
       uint64_t best = ~uint64_t(0);
       for (int32_t j = 0; j < c->slots; ++j) {
         const uint64_t t = c->expert_of[j] < 0 ? 0 : c->last_use[j];
-        if (t < now && t < best) {
+        if (t < first && t < best) {
           best = t;
           v = j;
         }

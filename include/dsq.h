@@ -341,8 +341,8 @@ typedef struct dsq_expert_cache {
   int32_t slots;               /* = gate.batch                                */
   int32_t* slot_of;            /* [E]: slot holding expert e, or -1           */
   int32_t* expert_of;          /* [slots]: expert in slot s, or -1            */
-  uint64_t* last_use;          /* [slots]: call stamp of the last use         */
-  uint64_t clock;              /* calls so far                                */
+  uint64_t* last_use;          /* [slots]: request stamp of the last use      */
+  uint64_t clock;              /* requests so far                             */
   uint64_t hits, misses, bytes_copied;
 } dsq_expert_cache;
 
@@ -360,8 +360,9 @@ dsq_status dsq_expert_cache_init(dsq_expert_cache* cache, const dsq_qweight* gat
  * dsq_expert_cache_plan -- host only, no GPU call: map n requested experts
  * (host [n]) to slots (slot_out host [n]) as one call.  A requested expert
  * already in a slot is a hit; a miss takes an empty slot (lowest index)
- * or else the least recently used slot not used in this call (ties: lowest
- * index), and is reported in fill_expert/fill_slot (host [n] each, *n_fill
+ * or else the least recently used slot not used in this call; every request,
+ * hit or miss, stamps its slot in request order.  Misses are reported in
+ * fill_expert/fill_slot (host [n] each, *n_fill
  * entries written, in request order).  Errors: DSQ_ERR_INVALID_ARG (NULL,
  * n < 0, an expert out of 0..E-1), DSQ_ERR_UNSUPPORTED (one call needs more
  * distinct experts than there are slots; the tables stay consistent, the

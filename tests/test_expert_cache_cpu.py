@@ -15,7 +15,7 @@ from group_quantized_moe_dsq_amd import dsq
 class LruModel:
     """Per call: a requested expert already in a slot is a hit; a miss takes
     an empty slot (lowest index) or the least recently used slot not used in
-    this call (ties: lowest index)."""
+    this call.  Every request stamps its slot in request order."""
 
     def __init__(self, E, slots):
         self.slot_of = [-1] * E
@@ -25,17 +25,18 @@ class LruModel:
         self.hits = self.misses = 0
 
     def call(self, experts):
-        self.clock += 1
-        now = self.clock
+        first = self.clock + 1
         out, fills = [], []
         for e in experts:
+            self.clock += 1
+            now = self.clock
             s = self.slot_of[e]
             if s >= 0:
                 self.hits += 1
             else:
                 cands = [(0 if self.expert_of[j] < 0 else self.last[j], j)
                          for j in range(len(self.expert_of))]
-                cands = [c for c in cands if c[0] < now]
+                cands = [c for c in cands if c[0] < first]
                 if not cands:
                     raise RuntimeError("working set larger than the cache")
                 _, s = min(cands)
