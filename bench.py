@@ -123,8 +123,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the hot path has no multi-GPU leg to run).", file=sys.stderr)
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the library's hot path runs on one device; it has no multi-GPU leg).",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
