@@ -61,6 +61,31 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
   return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const int lo = int(uint32_t(v)), hi = int(uint32_t(v >> 32));
+  const uint32_t a = uint32_t(__builtin_amdgcn_update_dpp(lo, lo, CTRL, 0xf, 0xf, false));
+  const uint32_t b = uint32_t(__builtin_amdgcn_update_dpp(hi, hi, CTRL, 0xf, 0xf, false));
+  return (uint64_t(b) << 32) | a;
+}
+
+// The key of lane (lane ^ m).  Inside a 16-lane row the data-parallel
+// primitives do it without the LDS crossbar: xor 1 and 2 are quad permutes,
+// xor 8 the row rotation by 8, xor 4 the row shifts by 4 (lanes with bit 2
+// clear read lane + 4, the others lane - 4); xor 16 and 32 go through
+// ds_bpermute.  m is a constant after unrolling, so one branch remains.
+__device__ __forceinline__ uint64_t xchg64(uint64_t v, int m, int lane) {
+  if (m == 1) return dpp64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  if (m == 2) return dpp64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  if (m == 8) return dpp64<0x128>(v);  // row_ror:8
+  if (m == 4) {
+    const uint64_t up = dpp64<0x104>(v);  // row_shl:4 -> lane + 4
+    const uint64_t dn = dpp64<0x114>(v);  // row_shr:4 -> lane - 4
+    return (lane & 4) ? dn : up;
+  }
+  return shfl_xor64(v, m);
+}
+
 // One round, bitonic path.  FROM_Y: the input is the logits (keys are formed
 // here), else the previous round's keys.  FINAL (one workgroup): write the k
 // best as (index, value); else write them as keys to out[block][k].
@@ -69,7 +94,7 @@ __device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
 // 2t + 1 (a wave owns 128 consecutive positions).  Every step of the network
 // (blocks of `size` sorted in alternating direction, the last one descending)
 // pairs position p with p ^ stride: stride 1 is inside a thread, strides 2 ..
-// 64 pair lanes of one wave (a lane exchange), and only strides 128 .. 512
+// 64 pair lanes of one wave (a lane exchange, xchg64), and only strides 128 .. 512
 // (6 of the 55 steps) go through LDS, each with one barrier (two LDS buffers
 // alternate, so a step's writes never meet the previous step's reads).  Both
 // members of a pair compute their new key from the same two keys: the lower
@@ -104,7 +129,7 @@ __global__ __launch_bounds__(kHeadSortThreads) void head_round_kernel(const floa
         o[1] = v[0];
       } else if (stride <= 64) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) o[b] = shfl_xor64(v[b], stride >> 1);
+        for (int b = 0; b < 2; ++b) o[b] = xchg64(v[b], stride >> 1, t & 63);
       } else {
         s[buf][2 * t] = v[0];
         s[buf][2 * t + 1] = v[1];
