@@ -112,7 +112,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-secondary", action="store_true")
-    ap.add_argument("--cases", default="head,gemv8,gemv4,sb4,sb4vocab,moe1,block1,cache,moe32,"
+    ap.add_argument("--cases", default="head,gemv8,gemv4,sb4,gemv4vocab,sb4vocab,moe1,block1,"
+                                       "cache,moe32,"
                                        "gemm256,moe256",
                     help="secondary workloads to run (comma list)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -274,24 +275,28 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
     if "sb4" in cases:
         rotated_gemv(4, 256, "super-block 4-bit GEMV 4096x4096 (M=1)", 64)
     torch.cuda.empty_cache()
-    if "sb4vocab" in cases:
-        # the vocab projection in the super-block format: 298 MB, cold by size
+    def vocab_gemv(bits, group, name):
+        # the vocab projection, 298-331 MB: cold by size
         NV = N_VOCAB
         w = synth.normal((NV, K), 0.02, 0, synth.W, 2, device=dev)
-        q = dsq.QWeight(4, 256, K, NV)
+        q = dsq.QWeight(bits, group, K, NV)
         dsq.pack_weights(w, q)
         del w
         torch.cuda.empty_cache()
         y = torch.empty(NV, device=dev)
         ms = time_calls(lambda i: dsq.gemv(q, x, y), 100, 1, torch)
-        b = qbytes(4, 256, K, NV) + K * 4 + NV * 4
+        b = qbytes(bits, group, K, NV) + K * 4 + NV * 4
         gbs = b / (ms * 1e-3) / 1e9
-        out.append({"workload": "super-block 4-bit vocab GEMV 4096x129280 (M=1)",
-                    "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+        out.append({"workload": name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": b})
         log(out[-1])
         del q
         torch.cuda.empty_cache()
+
+    if "gemv4vocab" in cases:
+        vocab_gemv(4, 64, "INT4 g64 vocab GEMV 4096x129280 (M=1)")
+    if "sb4vocab" in cases:
+        vocab_gemv(4, 256, "super-block 4-bit vocab GEMV 4096x129280 (M=1)")
 
     # MoE decode layers: 256 experts, H=4096, I=2048, top-6
     def build_moe(bits, group, bias_std):

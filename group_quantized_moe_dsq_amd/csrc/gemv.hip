@@ -19,6 +19,8 @@
 //   * R rows per wave step; their partial sums are reduced across the wave in
 //     one reduce-scatter, after which R lanes store the R outputs.  The next
 //     step's loads are issued before the current step's arithmetic.
+#include <algorithm>
+
 #include "common.h"
 #include "gemv_core.h"
 #include "head_key.h"
@@ -37,7 +39,10 @@ namespace dsq {
 #define DSQ_GEMV_WAVES_PER_CU 8
 #endif
 #ifndef DSQ_GEMV_WAVES_PER_CU_LARGE
-#define DSQ_GEMV_WAVES_PER_CU_LARGE 4  // when every wave gets >= 4 row blocks at the above
+#define DSQ_GEMV_WAVES_PER_CU_LARGE 4  // INT8, when every wave gets >= 4 row blocks at the above
+#endif
+#ifndef DSQ_GEMV_WAVES_PER_CU_LARGE4
+#define DSQ_GEMV_WAVES_PER_CU_LARGE4 8  // the same for INT4
 #endif
 
 template <int BITS, int R, int KCH>
@@ -222,20 +227,25 @@ __global__ __launch_bounds__(256) void gemv_kernel_long(const uint8_t* __restric
 
 namespace {
 
-// Waves launched (grid-stride beyond): large matrices run fewer, longer
+// Waves launched (grid-stride beyond): large INT8 matrices run fewer, longer
 // waves, each staging x once and keeping its prefetch pipeline full for
 // more row blocks (vocab projection: 87.8 against 90.6 us); small ones keep
-// every row block's loads in flight at once.
+// every row block's loads in flight at once.  INT4 does about twice the
+// arithmetic per byte, and two waves per SIMD hide it behind each other's
+// loads (INT4 g64 vocab projection: 56.5 against 65-67 us with one).
+template <int BITS>
 int max_waves(int rowblocks) {
   const int small = 256 * DSQ_GEMV_WAVES_PER_CU;
-  return rowblocks >= 4 * small ? 256 * DSQ_GEMV_WAVES_PER_CU_LARGE : small;
+  const int large = 256 * (BITS == 8 ? DSQ_GEMV_WAVES_PER_CU_LARGE : DSQ_GEMV_WAVES_PER_CU_LARGE4);
+  return rowblocks >= 4 * small ? large : small;
 }
 
 template <int BITS, int R, int KCH>
 hipError_t go(const QMat& q, const float* x, float* y, int N, int K, int group,
               uint64_t* wkey, int64_t* nkeys, hipStream_t stream) {
   const int rowblocks = (N + R - 1) / R;
-  const int waves = rowblocks < max_waves(rowblocks) ? rowblocks : max_waves(rowblocks);
+  const int waves =
+      rowblocks < max_waves<BITS>(rowblocks) ? rowblocks : max_waves<BITS>(rowblocks);
   const int blocks = (waves + 3) / 4;
   if (wkey) {
     hipLaunchKernelGGL((gemv_argmax_kernel<BITS, R, KCH>), dim3(blocks), dim3(256),
@@ -252,7 +262,8 @@ template <int BITS, int R>
 hipError_t go_long(const QMat& q, const float* x, float* y, int N, int K, int group,
                    hipStream_t stream) {
   const int rowblocks = (N + R - 1) / R;
-  const int waves = rowblocks < max_waves(rowblocks) ? rowblocks : max_waves(rowblocks);
+  const int waves =
+      rowblocks < max_waves<BITS>(rowblocks) ? rowblocks : max_waves<BITS>(rowblocks);
   const int blocks = (waves + 3) / 4;
   hipLaunchKernelGGL((gemv_kernel_long<BITS, R>), dim3(blocks), dim3(256), 0, stream, q.payload,
                      q.meta, x, y, N, K, group);
@@ -294,9 +305,9 @@ bool gemv_argmax_supported(const dsq_qweight& W) {
 }
 
 size_t gemv_argmax_key_bytes() {
-  const int most = 256 * (DSQ_GEMV_WAVES_PER_CU > DSQ_GEMV_WAVES_PER_CU_LARGE
-                              ? DSQ_GEMV_WAVES_PER_CU
-                              : DSQ_GEMV_WAVES_PER_CU_LARGE);
+  const int most = 256 * std::max(DSQ_GEMV_WAVES_PER_CU,
+                                  std::max(DSQ_GEMV_WAVES_PER_CU_LARGE,
+                                           DSQ_GEMV_WAVES_PER_CU_LARGE4));
   return size_t(align256(int64_t(most + 3) * 8));
 }
 

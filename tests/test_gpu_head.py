@@ -111,7 +111,7 @@ def test_gemv_topk_vocab_full_size(k):
 # per lane, and a row length past that (the separate selection pass)
 @pytest.mark.parametrize("nbits,group,N,K", [(8, 64, 1, 256), (4, 64, 37, 512), (8, 128, 1000, 4096),
                                             (4, 128, 5003, 8192), (8, 64, 4097, 2048),
-                                            (8, 64, 300, 12288)])
+                                            (8, 64, 300, 12288), (4, 64, 129280, 4096)])
 def test_gemv_top1_matches_selection_on_its_logits(nbits, group, N, K):
     say(f"gemv top-1 bits={nbits} group={group} N={N} K={K}")
     w = synth.normal((N, K), 0.02, 0, synth.W, 60 + N, device="cuda")

@@ -144,21 +144,23 @@ def test_gemv_one_hot_returns_dequantized_columns():
             np.testing.assert_array_equal(y, cols[:, k])
 
 
-def test_gemv_vocab_projection_full_size_sampled():
-    """INT8 group-64 vocab projection K=4096, N=129280 (the whole matrix is
-    packed and multiplied on the GPU); 1024 sampled rows are checked against
-    the oracle, whose codes for those rows are recomputed from the same fp32
-    weights (rows quantize independently)."""
-    say("gemv vocab 129280 x 4096 INT8 g64")
+@pytest.mark.parametrize("bits,group", [(8, 64), (4, 64), (4, 128)])
+def test_gemv_vocab_projection_full_size_sampled(bits, group):
+    """Vocab projection K=4096, N=129280 (the whole matrix is packed and
+    multiplied on the GPU, in the large-matrix launch shape: every wave runs
+    many row blocks); 1024 sampled rows are checked against the oracle, whose
+    codes for those rows are recomputed from the same fp32 weights (rows
+    quantize independently)."""
+    say(f"gemv vocab 129280 x 4096 bits={bits} g{group}")
     N, K = 129280, 4096
     w = synth.normal((N, K), 0.02, 0, synth.W, 2, device="cuda")
     x = synth.normal((K,), 1.0, 0, synth.X, 2, device="cuda")
-    qw = pack_gpu(w, 8, 64)
+    qw = pack_gpu(w, bits, group)
     y = dsq.gemv(qw, x).cpu().numpy()
     rows = np.sort(np.random.default_rng(53).choice(N, 1024, replace=False))
     rows[-1] = N - 1
     wr = w[torch.from_numpy(rows).cuda()].cpu().numpy()
-    m = oracle.quantize(wr, 8, 64)
+    m = oracle.quantize(wr, bits, group)
     ref, S = oracle.qmatmul_ref(x.cpu().numpy()[None, :], m)
     assert_bounded(y[rows], ref[0], 1e-5 * S[0], "vocab gemv sampled rows")
     # the packed codes of those rows are the oracle's
