@@ -33,7 +33,7 @@ namespace dsq {
 #define DSQ_GEMV_R8 2  // rows per wave step, INT8
 #endif
 #ifndef DSQ_GEMV_R4
-#define DSQ_GEMV_R4 4  // rows per wave step, INT4
+#define DSQ_GEMV_R4 2  // rows per wave step, INT4
 #endif
 #ifndef DSQ_GEMV_WAVES_PER_CU
 #define DSQ_GEMV_WAVES_PER_CU 8
@@ -42,7 +42,7 @@ namespace dsq {
 #define DSQ_GEMV_WAVES_PER_CU_LARGE 4  // INT8, when every wave gets >= 4 row blocks at the above
 #endif
 #ifndef DSQ_GEMV_WAVES_PER_CU_LARGE4
-#define DSQ_GEMV_WAVES_PER_CU_LARGE4 8  // the same for INT4
+#define DSQ_GEMV_WAVES_PER_CU_LARGE4 12  // the same for INT4 (three workgroups per CU)
 #endif
 
 template <int BITS, int R, int KCH>
@@ -231,8 +231,9 @@ namespace {
 // waves, each staging x once and keeping its prefetch pipeline full for
 // more row blocks (vocab projection: 87.8 against 90.6 us); small ones keep
 // every row block's loads in flight at once.  INT4 does about twice the
-// arithmetic per byte, and two waves per SIMD hide it behind each other's
-// loads (INT4 g64 vocab projection: 56.5 against 65-67 us with one).
+// arithmetic per byte; with two rows per step (167 VGPRs) three waves fit a
+// SIMD and hide it behind each other's loads (INT4 g64 vocab projection:
+// 55.5-55.8 us, against 65-67 us with one wave of four rows per SIMD).
 template <int BITS>
 int max_waves(int rowblocks) {
   const int small = 256 * DSQ_GEMV_WAVES_PER_CU;
