@@ -13,7 +13,9 @@ more than the 256 MB Infinity Cache, so no input stays cached across steps.
 HIP events on the stream it runs on.  `secondary` reports the other workloads
 (INT8 GEMV, MoE decode, batched MoE decode, dense and MoE prefill) with
 their own timings; `cpu_baseline` times the CPU oracle (the pages' own
-OpenMP fused-dequant loop) on a bounded sample of the headline workload.
+OpenMP fused-dequant loop) on the whole headline workload, in a child process
+after the GPU phase, pinned one thread per physical core with one core left
+to the GPU thread.
 
     python bench.py [--gpus 1] [--steps 200] [--warmup 20]
 """
@@ -121,8 +123,13 @@ def main():
                     help="only run a plain device copy of 1 GiB a few times: the reference "
                          "kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE "
                          "counters")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-reps", type=int, default=5,
+                    help="timed passes of the CPU baseline (median reported)")
+    ap.add_argument("--cpu-child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.cpu_child:
+        cpu_baseline_child(args.cpu_reps)
+        return
     if args.gpus != 1:
         print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
               "(the library's hot path runs on one device; it has no multi-GPU leg).",
@@ -242,7 +249,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds, np)
+        result["cpu_baseline"] = cpu_baseline(args.cpu_reps)
     print(json.dumps(result), flush=True)
 
 
@@ -442,42 +449,108 @@ def dense_prefill(dsq, synth, torch, dev):
 
 
 
-def cpu_baseline(seconds, np):
-    """The oracle's fp32 fused-dequant OpenMP GEMV (the pages' CPU method) on
-    a bounded sample of the headline workload: the whole INT4 4096x4096
-    matrix plus the first 16384 rows of the INT8 vocab matrix."""
+def cpu_topology():
+    """Physical cores this process may use, read at run time: the CPUs in the
+    affinity mask grouped by (package, core), capped by the cgroup's CPU
+    quota; one is left to the thread that drives the GPU ("Running a
+    284B-parameter LLM from 3.2 GB of RAM in plain C": CPU matmul throughput
+    collapsed while the GPU thread competed for cores), and hyperthreads are
+    not used ("Hand-writing a DeepSeek inference engine in pure C" §4.2: 32
+    threads on 16 cores ran ~10% slower than 16)."""
+    cpus = sorted(os.sched_getaffinity(0))
+    cores = set()
+    for c in cpus:
+        base = f"/sys/devices/system/cpu/cpu{c}/topology/"
+        try:
+            with open(base + "physical_package_id") as fh:
+                pkg = fh.read().strip()
+            with open(base + "core_id") as fh:
+                core = fh.read().strip()
+            cores.add((pkg, core))
+        except OSError:
+            cores.add(("?", str(c)))
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as fh:
+            q, per = fh.read().split()[:2]
+            if q != "max":
+                quota = max(1, -(-int(q) // int(per)))
+    except (OSError, ValueError):
+        pass
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    physical = len(cores) if quota is None else min(len(cores), quota)
+    return {"cpu_model": model, "logical_cpus": len(cpus), "physical_cores": physical,
+            "cgroup_cpu_quota": quota, "threads": max(1, physical - 1)}
+
+
+def cpu_baseline_child(reps):
+    """Runs in its own process (OpenMP pinned by the parent's environment):
+    the oracle's fp32 fused-dequant OpenMP GEMV (the pages' CPU method) on the
+    whole headline workload, one warm-up pass, then the median of `reps`."""
+    import statistics
+
     import oracle
     from group_quantized_moe_dsq_amd import synth
 
-    threads = max(1, (os.cpu_count() or 2) - 1)
-    threads = min(threads, 16)
-    oracle.set_threads(threads)
-    K = 4096
-    rows_v = 16384
+    K, NV = N_EMBD, N_VOCAB
+    # the same shapes, seeds and distributions as the GPU phase, drawn with
+    # the CPU generator
     w4 = synth.normal((4096, K), 0.02, 0, synth.W, 21).numpy()
-    wv = synth.normal((rows_v, K), 0.02, 0, synth.W, 22).numpy()
     m4 = oracle.quantize(w4, 4, 64)
+    del w4
+    wv = synth.normal((NV, K), 0.02, 0, synth.W, 22).numpy()
     mv = oracle.quantize(wv, 8, 64)
-    del w4, wv
+    del wv
     x = synth.normal((1, K), 1.0, 0, synth.X, 21).numpy()
-    sample_bytes = qbytes(4, 64, K, 4096) + qbytes(8, 64, K, rows_v) + 2 * K * 4 + \
-        (4096 + rows_v) * 4
-    oracle.qmatmul_f32(x, m4)
-    oracle.qmatmul_f32(x, mv)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
+    step_bytes = qbytes(4, 64, K, 4096) + qbytes(8, 64, K, NV) + 2 * K * 4 + (4096 + NV) * 4
+
+    def step():
         oracle.qmatmul_f32(x, m4)
         oracle.qmatmul_f32(x, mv)
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = (time.perf_counter() - t0) / n
-    return {"value": round(sample_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"INT4 g64 4096x4096 + first {rows_v} rows of the INT8 g64 vocab matrix, "
-                      f"M=1; {n} passes in {seconds:.0f} s; fp32 fused dequant, OpenMP "
-                      f"{threads} threads"}
+
+    step()
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        step()
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    print(json.dumps({"ms_per_step": med * 1e3, "times_ms": [t * 1e3 for t in times],
+                      "step_bytes": step_bytes, "threads": oracle.max_threads()}), flush=True)
+
+
+def cpu_baseline(reps):
+    """The CPU oracle timed on the host's physical cores in a phase after the
+    GPU phase (never concurrently with GPU work), in a child process pinned
+    with OMP_PROC_BIND=close / OMP_PLACES=cores."""
+    import subprocess
+
+    topo = cpu_topology()
+    env = dict(os.environ, OMP_NUM_THREADS=str(topo["threads"]), OMP_PROC_BIND="close",
+               OMP_PLACES="cores")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-child",
+                        "--cpu-reps", str(reps)], env=env, capture_output=True, text=True,
+                       timeout=900)
+    if r.returncode != 0:
+        raise RuntimeError("cpu baseline child failed:\n" + r.stderr[-2000:])
+    rec = json.loads(r.stdout.strip().splitlines()[-1])
+    gbs = rec["step_bytes"] / (rec["ms_per_step"] * 1e-3) / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": rec["threads"], "kind": "oracle",
+            "sample": "the whole headline step (INT4 g64 4096x4096 + INT8 g64 4096x129280 GEMV, "
+                      f"M=1, {rec['step_bytes']} bytes), fp32 fused dequant, OpenMP "
+                      f"{rec['threads']} threads pinned one per physical core "
+                      "(OMP_PROC_BIND=close, OMP_PLACES=cores), one core left to the GPU "
+                      f"thread; 1 warm-up pass, median of {reps}",
+            "ms_per_step": round(rec["ms_per_step"], 3),
+            "times_ms": [round(t, 3) for t in rec["times_ms"]], **topo}
 
 
 if __name__ == "__main__":

@@ -1,19 +1,23 @@
 """Build libdsq.so (gfx950 only) in-tree with hipcc.
 
     python -m group_quantized_moe_dsq_amd.build
+
+Every source compiles to its own object (in parallel) under _build/, then one
+link step makes the shared library.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import os
 import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+OBJ = os.path.join(os.path.dirname(HERE), "_build")
 LIB = os.path.join(HERE, "libdsq.so")
 SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemv_sb4.hip", "decode.hip", "route.hip",
-           "gemm_mfma.hip",
-           "gmm.hip", "head.hip"]
+           "gemm_mfma.hip", "gmm.hip", "head.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -21,10 +25,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
-    # every symbol must resolve at link time: a kernel whose host stub was not
-    # emitted fails the build here instead of at load time
-    "-Wl,-z,defs",
     # IEEE fp32 division and sqrt: the quantizer's codes depend on it
     "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-fno-fast-math",
@@ -32,18 +32,36 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
 ]
+LINK = [
+    "--offload-arch=gfx950",
+    "-shared",
+    # every symbol must resolve at link time: a kernel whose host stub was not
+    # emitted fails the build here instead of at load time
+    "-Wl,-z,defs",
+]
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libdsq.so")
+        raise RuntimeError("hipcc failed: " + " ".join(cmd[-3:]))
+    return r
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    os.makedirs(OBJ, exist_ok=True)
+    objs = [os.path.join(OBJ, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
+    with cf.ThreadPoolExecutor(workers) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([HIPCC, *LINK, *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

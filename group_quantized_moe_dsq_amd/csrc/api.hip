@@ -118,7 +118,7 @@ int64_t moe_layout(void* ws, int64_t T, int32_t E, int32_t k, int64_t H, int64_t
   m.pos = static_cast<int32_t*>(c.take(nk, 4));
   m.active = static_cast<int32_t*>(c.take(E, 4));
   m.n_active = static_cast<int32_t*>(c.take(1, 4));
-  m.bitmap = static_cast<uint32_t*>(c.take(int64_t(E) * ((T + 31) / 32), 4));
+  m.bitmap = static_cast<uint32_t*>(c.take(int64_t(group_scratch_words(T, E)), 4));
   m.hbuf = c.take(nk * I, 4);
   m.ybuf = static_cast<float*>(c.take(nk * H, 4));
   // token tiles of the grouped GEMM: routed rows nk in at most min(nk, E) experts
@@ -265,6 +265,36 @@ dsq_status dsq_moe_route_topk(const float* logits, const float* bias, int64_t T,
   dsq_status s = check_device();
   if (s != DSQ_OK) return s;
   return hip_status(launch_topk(logits, bias, T, E, top_k, idx, weights, (hipStream_t)stream));
+}
+
+size_t dsq_moe_group_workspace_bytes(int64_t T, int32_t E, int32_t top_k) {
+  if (T < 0 || E <= 0 || top_k <= 0 || top_k > E) return 0;
+  if (T > 65536 || E > 4096 || top_k > 32) return 0;
+  // bitmap (+ prefixes), active list, its count
+  return size_t(align256(int64_t(group_scratch_words(T, E)) * 4) + align256(int64_t(E) * 4) +
+                align256(4));
+}
+
+dsq_status dsq_moe_group(const int32_t* idx, int64_t T, int32_t E, int32_t top_k,
+                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!counts || !offsets || (T > 0 && (!idx || !perm || !pos))) return DSQ_ERR_INVALID_ARG;
+  if (T < 0 || E <= 0 || top_k <= 0 || top_k > E) return DSQ_ERR_SHAPE;
+  if (T > 65536 || E > 4096 || top_k > 32) return DSQ_ERR_UNSUPPORTED;
+  if ((idx && !aligned(idx, 4)) || !aligned(counts, 4) || !aligned(offsets, 4) ||
+      (perm && !aligned(perm, 4)) || (pos && !aligned(pos, 4)))
+    return DSQ_ERR_ALIGN;
+  const size_t need = dsq_moe_group_workspace_bytes(T, E, top_k);
+  if (!workspace || workspace_bytes < need) return DSQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return DSQ_ERR_ALIGN;
+  dsq_status s = check_device();
+  if (s != DSQ_OK) return s;
+  Carver c(workspace);
+  uint32_t* scratch = static_cast<uint32_t*>(c.take(int64_t(group_scratch_words(T, E)), 4));
+  int32_t* active = static_cast<int32_t*>(c.take(E, 4));
+  int32_t* n_active = static_cast<int32_t*>(c.take(1, 4));
+  return hip_status(launch_group(idx, T, top_k, E, scratch, counts, offsets, perm, pos, active,
+                                 n_active, 1, nullptr, nullptr, (hipStream_t)stream));
 }
 
 size_t dsq_topk_workspace_bytes(int64_t N, int32_t k) {

@@ -9,6 +9,21 @@
 namespace dsq {
 
 constexpr int kWave = 64;
+constexpr int kMaxCus = 256;  // MI355X; grids sized per CU never assume more
+
+// Compute units of the current device, read once per device.
+inline int device_cus() {
+  static int cache[64] = {0};
+  int d = 0;
+  if (hipGetDevice(&d) != hipSuccess || d < 0 || d >= 64) return kMaxCus;
+  if (cache[d] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess || n <= 0)
+      n = kMaxCus;
+    cache[d] = n;
+  }
+  return cache[d];
+}
 
 __host__ __device__ inline int64_t align256(int64_t b) { return (b + 255) & ~int64_t(255); }
 

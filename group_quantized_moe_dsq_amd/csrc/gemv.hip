@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void gemv_kernel(const uint8_t* __restrict__ p
   const int lane = threadIdx.x & 63;
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int nwaves = (gridDim.x * blockDim.x) >> 6;
-  const int row_bytes = K * BITS / 8;
+  const int row_bytes = K / 8 * BITS;  // K is a multiple of the group
   const int nchunk = row_bytes / 16;
   const int groups = K / group;
 
@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256) void gemv_argmax_kernel(const uint8_t* __restr
   const int lane = threadIdx.x & 63;
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int nwaves = (gridDim.x * blockDim.x) >> 6;
-  const int row_bytes = K * BITS / 8;
+  const int row_bytes = K / 8 * BITS;  // K is a multiple of the group
   const int nchunk = row_bytes / 16;
   const int groups = K / group;
 
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void gemv_kernel_long(const uint8_t* __restric
   const int lane = threadIdx.x & 63;
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int nwaves = (gridDim.x * blockDim.x) >> 6;
-  const int row_bytes = K * BITS / 8;
+  const int row_bytes = K / 8 * BITS;  // K is a multiple of the group
   const int nchunk = row_bytes / 16;
   const int groups = K / group;
   for (int rb = wave; rb * R < N; rb += nwaves) {
@@ -234,19 +234,39 @@ namespace {
 // arithmetic per byte; with two rows per step (167 VGPRs) three waves fit a
 // SIMD and hide it behind each other's loads (INT4 g64 vocab projection:
 // 55.5-55.8 us, against 65-67 us with one wave of four rows per SIMD).
+// The grid is sized from the device's compute units (at most 256, the size
+// the top-1 key workspace is built for) and, for large matrices, from the
+// number of 4-wave workgroups per CU the compiled kernel actually fits
+// (`occ`, from its register and LDS use): a grid that asked for more would
+// run its last workgroups as a second round.
 template <int BITS>
-int max_waves(int rowblocks) {
-  const int small = 256 * DSQ_GEMV_WAVES_PER_CU;
-  const int large = 256 * (BITS == 8 ? DSQ_GEMV_WAVES_PER_CU_LARGE : DSQ_GEMV_WAVES_PER_CU_LARGE4);
+int max_waves(int rowblocks, int occ) {
+  const int cus = std::min(device_cus(), kMaxCus);
+  const int small = cus * DSQ_GEMV_WAVES_PER_CU;
+  const int want = BITS == 8 ? DSQ_GEMV_WAVES_PER_CU_LARGE : DSQ_GEMV_WAVES_PER_CU_LARGE4;
+  const int large = cus * std::max(4, std::min(want, 4 * occ));
   return rowblocks >= 4 * small ? large : small;
+}
+
+// 4-wave workgroups of `kernel` resident per CU with `lds` bytes of LDS each.
+template <class Kernel>
+int occupancy(Kernel kernel, size_t lds) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 256, lds) != hipSuccess || n <= 0)
+    n = 1;
+  return n;
 }
 
 template <int BITS, int R, int KCH>
 hipError_t go(const QMat& q, const float* x, float* y, int N, int K, int group,
               uint64_t* wkey, int64_t* nkeys, hipStream_t stream) {
+  // the largest x this instance stages (KCH chunks of 16 bytes per lane)
+  constexpr size_t kLds = size_t(KCH) * 64 * Codes<BITS>::kPerChunk * 4;
+  static const int occ_plain = occupancy(gemv_kernel<BITS, R, KCH>, kLds);
+  static const int occ_key = occupancy(gemv_argmax_kernel<BITS, R, KCH>, kLds);
   const int rowblocks = (N + R - 1) / R;
-  const int waves =
-      rowblocks < max_waves<BITS>(rowblocks) ? rowblocks : max_waves<BITS>(rowblocks);
+  const int mw = max_waves<BITS>(rowblocks, wkey ? occ_key : occ_plain);
+  const int waves = rowblocks < mw ? rowblocks : mw;
   const int blocks = (waves + 3) / 4;
   if (wkey) {
     hipLaunchKernelGGL((gemv_argmax_kernel<BITS, R, KCH>), dim3(blocks), dim3(256),
@@ -262,9 +282,10 @@ hipError_t go(const QMat& q, const float* x, float* y, int N, int K, int group,
 template <int BITS, int R>
 hipError_t go_long(const QMat& q, const float* x, float* y, int N, int K, int group,
                    hipStream_t stream) {
+  static const int occ = occupancy(gemv_kernel_long<BITS, R>, 0);
   const int rowblocks = (N + R - 1) / R;
-  const int waves =
-      rowblocks < max_waves<BITS>(rowblocks) ? rowblocks : max_waves<BITS>(rowblocks);
+  const int mw = max_waves<BITS>(rowblocks, occ);
+  const int waves = rowblocks < mw ? rowblocks : mw;
   const int blocks = (waves + 3) / 4;
   hipLaunchKernelGGL((gemv_kernel_long<BITS, R>), dim3(blocks), dim3(256), 0, stream, q.payload,
                      q.meta, x, y, N, K, group);
@@ -276,7 +297,7 @@ hipError_t go_long(const QMat& q, const float* x, float* y, int N, int K, int gr
 template <int BITS>
 hipError_t dispatch(const QMat& q, const float* x, float* y, int N, int K, int group,
                     uint64_t* wkey, int64_t* nkeys, hipStream_t stream) {
-  const int nchunk = K * BITS / 8 / 16;
+  const int nchunk = K / 8 * BITS / 16;
   const int kch = (nchunk + 63) / 64;
   constexpr int R = BITS == 8 ? DSQ_GEMV_R8 : DSQ_GEMV_R4;
   switch (kch) {
@@ -306,7 +327,7 @@ bool gemv_argmax_supported(const dsq_qweight& W) {
 }
 
 size_t gemv_argmax_key_bytes() {
-  const int most = 256 * std::max(DSQ_GEMV_WAVES_PER_CU,
+  const int most = kMaxCus * std::max(DSQ_GEMV_WAVES_PER_CU,
                                   std::max(DSQ_GEMV_WAVES_PER_CU_LARGE,
                                            DSQ_GEMV_WAVES_PER_CU_LARGE4));
   return size_t(align256(int64_t(most + 3) * 8));

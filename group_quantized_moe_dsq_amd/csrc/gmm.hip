@@ -22,7 +22,10 @@
 // rounding only.
 //
 // Activations: the fp32 path splits every activation into two bf16 parts,
-// x = hi + lo with hi = bf16(x), lo = bf16(x - hi) (|x - hi - lo| <= 2^-18 |x|),
+// x = hi + lo with hi = bf16(x), lo = bf16(x - hi) (|x - hi - lo| <= 2^-17 |x|:
+// bf16 keeps 8 significant bits, so each round-to-nearest step leaves at most
+// 2^-8 of its input, and the second input is itself at most 2^-8 |x|, with
+// one bit to spare from the exponent step),
 // each part its own MFMA row, and adds the two rows' results at the end; the
 // bf16 path uses hi only.  A prep kernel writes the parts of every token tile
 // in MFMA operand order (one 16-byte load per lane and k step) together with

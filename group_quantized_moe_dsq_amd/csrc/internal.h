@@ -56,10 +56,15 @@ hipError_t launch_topk_parts(const float* parts, int nparts, const float* rbias,
                              int64_t T, int32_t E, int32_t k, int32_t* idx, float* w,
                              hipStream_t stream);
 
-// Stable grouping of the T*k routing entries by expert (one workgroup).
-// With tiles, also the token-tile table of the grouped GEMM for tiles of tpt
-// rows (Groups::tiles; at most gmm_tiles_bound(T*k, min(T*k, E), 16/tpt)).
-hipError_t launch_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, uint32_t* bitmap,
+// Stable grouping of the T*k routing entries by expert (E <= 4096): counts,
+// offsets, perm (entries in (expert, entry) order), pos (perm's inverse; -1
+// for an entry whose expert is outside [0, E)), the active experts.  With
+// tiles, also the token-tile table of the grouped GEMM for tiles of tpt rows
+// (Groups::tiles; at most gmm_tiles_bound(T*k, min(T*k, E), 16/tpt)).
+// scratch: group_scratch_words(T, E) 32-bit words (bitmap, and for many
+// tokens the per-expert popcount prefixes).
+size_t group_scratch_words(int64_t T, int32_t E);
+hipError_t launch_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, uint32_t* scratch,
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
                         int32_t* active, int32_t* n_active, int tpt, int4* tiles,
                         int32_t* n_tiles, hipStream_t stream);

@@ -432,15 +432,98 @@ hipError_t launch_topk_parts(const float* parts, int nparts, const float* rbias,
 
 // ---------------------------------------------------------------------------
 // Grouping by expert (§3.5 of the same page: gather the tokens routed to one
-// expert).  One workgroup.  A token selects distinct experts, so an entry's
-// rank inside its expert's segment is the number of earlier tokens that
-// selected the same expert: a bitmap [E][ceil(T/32)] with bit t of row e set
-// when token t chose e turns that into popcounts.  Integer only, so the
-// result is exact and stable (ascending token order within an expert).
+// expert).  A token selects distinct experts, so an entry's rank inside its
+// expert's segment is the number of earlier tokens that selected the same
+// expert.  A bitmap with bit t of expert e's row set when token t chose e
+// turns that into popcounts.  Integer only, so the result is exact and stable
+// (ascending token order within an expert).  Entries whose expert lies
+// outside [0, E) are not grouped (pos = -1).
 // With `tiles`, the same pass lists the grouped GEMM's token tiles: expert
 // segments cut into tiles of tpt rows, one record per tile in (active expert,
 // tile) order, written by the entry that opens the tile.
+// Up to kGroupSmallT tokens one workgroup does everything (the rank of an
+// entry popcounts at most 8 words); beyond that three kernels keep every
+// entry's rank O(1): per 32-token word the bitmap words of all experts, per
+// expert the exclusive prefix of the words' popcounts, then one thread per
+// entry.
 // ---------------------------------------------------------------------------
+constexpr int kGroupSmallT = 256;
+constexpr int kGroupMaxE = 4096;
+
+// Wave 0 scans the per-expert counts held in s_off[0..E): on return s_off[e]
+// is expert e's first position (s_off[E] the total), s_act[e] its rank among
+// the experts with entries and s_tile[e] its first token tile (tiles of ntpt
+// rows).  With `out`, the offsets, active list and their totals (and the
+// counts, when `counts` is not NULL) are written to memory as well.  The
+// caller synchronises before and after.
+__device__ void group_scan_experts(int E, int ntpt, int32_t* s_off, int32_t* s_act,
+                                   int32_t* s_tile, bool out, int32_t* counts, int32_t* offsets,
+                                   int32_t* active, int32_t* n_active, int32_t* n_tiles) {
+  if (threadIdx.x >= 64) return;
+  const int lane = threadIdx.x;
+  const int per = (E + 63) / 64;
+  const int lo = min(lane * per, E);
+  const int hi = min(lo + per, E);
+  int sc = 0, sa = 0, st = 0;
+  for (int e = lo; e < hi; ++e) {
+    sc += s_off[e];
+    sa += s_off[e] > 0;
+    st += (s_off[e] + ntpt - 1) / ntpt;
+  }
+  int ic = sc, ia = sa, it = st;  // inclusive scan across lanes
+  for (int o = 1; o < 64; o <<= 1) {
+    const int uc = __shfl_up(ic, o);
+    const int ua = __shfl_up(ia, o);
+    const int ut = __shfl_up(it, o);
+    if (lane >= o) {
+      ic += uc;
+      ia += ua;
+      it += ut;
+    }
+  }
+  int rc = ic - sc, ra = ia - sa, rt = it - st;
+  for (int e = lo; e < hi; ++e) {
+    const int c = s_off[e];
+    s_off[e] = rc;
+    s_act[e] = ra;
+    s_tile[e] = rt;
+    if (out) {
+      if (counts) counts[e] = c;
+      offsets[e] = rc;
+      if (c > 0) active[ra] = e;
+    }
+    rc += c;
+    ra += c > 0;
+    rt += (c + ntpt - 1) / ntpt;
+  }
+  if (lane == 63) {
+    s_off[E] = ic;
+    if (out) {
+      offsets[E] = ic;
+      *n_active = ia;
+      if (n_tiles) *n_tiles = it;
+    }
+  }
+}
+
+// Places entry j = t * k + i of expert e at rank `rank` of its segment, and
+// writes the token-tile record when the entry opens a tile.
+__device__ __forceinline__ void group_place(int j, int e, int rank, const int32_t* s_off,
+                                            const int32_t* s_act, const int32_t* s_tile,
+                                            int tpt, int32_t* perm, int32_t* pos, int4* tiles) {
+  const int p = s_off[e] + rank;
+  perm[p] = j;
+  pos[j] = p;
+  // the activation tile index is the one the grouped GEMM's prep assigns
+  // (segment start / tpt + active rank + tile)
+  if (tiles && rank % tpt == 0) {
+    const int c = s_off[e + 1] - s_off[e];
+    const int t = rank / tpt;
+    tiles[s_tile[e] + t] = make_int4(e, p, min(tpt, c - rank), s_off[e] / tpt + s_act[e] + t);
+  }
+}
+
+// Few tokens: one workgroup; bitmap [E][ceil(T/32)], built with atomics.
 __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__ idx, int T, int k,
                                                      int E, uint32_t* __restrict__ bm,
                                                      int32_t* __restrict__ counts,
@@ -451,9 +534,9 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__
                                                      int32_t* __restrict__ n_active, int tpt,
                                                      int4* __restrict__ tiles,
                                                      int32_t* __restrict__ n_tiles) {
-  __shared__ int32_t s_off[4097];
-  __shared__ int32_t s_act[4097];
-  __shared__ int32_t s_tile[4097];
+  __shared__ int32_t s_off[kGroupMaxE + 1];
+  __shared__ int32_t s_act[kGroupMaxE + 1];
+  __shared__ int32_t s_tile[kGroupMaxE + 1];
   const int W = (T + 31) / 32;
   const int nent = T * k;
   for (int i = threadIdx.x; i < E * W; i += blockDim.x) bm[i] = 0u;
@@ -461,7 +544,7 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__
   for (int j = threadIdx.x; j < nent; j += blockDim.x) {
     const int e = idx[j];
     const int t = j / k;
-    atomicOr(&bm[e * W + (t >> 5)], 1u << (t & 31));
+    if (unsigned(e) < unsigned(E)) atomicOr(&bm[e * W + (t >> 5)], 1u << (t & 31));
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
@@ -471,80 +554,133 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__
     s_off[e] = c;
   }
   __syncthreads();
-  // exclusive scans of counts, of (count > 0) and of token tiles by wave 0
-  const int ntpt = tiles ? tpt : 1;
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
-    const int per = (E + 63) / 64;
-    const int lo = lane * per;
-    const int hi = min(lo + per, E);
-    int sc = 0, sa = 0, st = 0;
-    for (int e = lo; e < hi; ++e) {
-      sc += s_off[e];
-      sa += s_off[e] > 0;
-      st += (s_off[e] + ntpt - 1) / ntpt;
-    }
-    int ic = sc, ia = sa, it = st;  // inclusive scan across lanes
-    for (int o = 1; o < 64; o <<= 1) {
-      const int uc = __shfl_up(ic, o);
-      const int ua = __shfl_up(ia, o);
-      const int ut = __shfl_up(it, o);
-      if (lane >= o) {
-        ic += uc;
-        ia += ua;
-        it += ut;
-      }
-    }
-    int rc = ic - sc, ra = ia - sa, rt = it - st;
-    for (int e = lo; e < hi; ++e) {
-      const int c = s_off[e];
-      counts[e] = c;
-      s_off[e] = rc;
-      s_act[e] = ra;
-      s_tile[e] = rt;
-      offsets[e] = rc;
-      if (c > 0) active[ra] = e;
-      rc += c;
-      ra += c > 0;
-      rt += (c + ntpt - 1) / ntpt;
-    }
-    if (lane == 63) {
-      offsets[E] = ic;
-      s_off[E] = ic;
-      *n_active = ia;
-      if (tiles) *n_tiles = it;
-    }
-  }
+  group_scan_experts(E, tiles ? tpt : 1, s_off, s_act, s_tile, true, counts, offsets, active,
+                     n_active, tiles ? n_tiles : nullptr);
   __syncthreads();
   for (int j = threadIdx.x; j < nent; j += blockDim.x) {
     const int e = idx[j];
+    if (unsigned(e) >= unsigned(E)) {
+      pos[j] = -1;
+      continue;
+    }
     const int t = j / k;
     // the bitmap was built with device-scope atomics: read it past L1
     const volatile uint32_t* row = bm + e * W;
     int rank = 0;
     for (int w = 0; w < (t >> 5); ++w) rank += __popc(row[w]);
     rank += __popc(row[t >> 5] & ((1u << (t & 31)) - 1u));
-    const int p = s_off[e] + rank;
-    perm[p] = j;
-    pos[j] = p;
-    // the entry that opens a token tile writes the tile's record; the
-    // activation tile index is the one the grouped GEMM's prep assigns
-    // (segment start / tpt + active rank + tile)
-    if (tiles && rank % tpt == 0) {
-      const int c = s_off[e + 1] - s_off[e];
-      const int t = rank / tpt;
-      tiles[s_tile[e] + t] = make_int4(e, p, min(tpt, c - rank), s_off[e] / tpt + s_act[e] + t);
-    }
+    group_place(j, e, rank, s_off, s_act, s_tile, tpt, perm, pos, tiles);
   }
 }
 
-hipError_t launch_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, uint32_t* bitmap,
+// Many tokens, step 1: one workgroup per 32-token word w writes the bitmap
+// words bm[w][e] of every expert (LDS atomics, then plain stores: no
+// clearing pass, every word is written once).
+__global__ __launch_bounds__(256) void group_bits_kernel(const int32_t* __restrict__ idx, int T,
+                                                         int k, int E,
+                                                         uint32_t* __restrict__ bm) {
+  __shared__ uint32_t bits[kGroupMaxE];
+  const int w = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) bits[e] = 0u;
+  __syncthreads();
+  const int j0 = w * 32 * k, j1 = min(T, (w + 1) * 32) * k;
+  for (int j = j0 + threadIdx.x; j < j1; j += blockDim.x) {
+    const int e = idx[j];
+    if (unsigned(e) < unsigned(E)) atomicOr(&bits[e], 1u << ((j / k) & 31));
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) bm[int64_t(w) * E + e] = bits[e];
+}
+
+// Step 2: per expert, the exclusive prefix over the words of their
+// popcounts, pre[w][e], and the expert's count.  A workgroup owns 64 experts
+// (one per lane); its 16 waves split the words into 16 consecutive ranges.
+constexpr int kGroupPrefixWaves = 16;
+__global__ __launch_bounds__(1024) void group_prefix_kernel(const uint32_t* __restrict__ bm,
+                                                            int W, int E,
+                                                            int32_t* __restrict__ pre,
+                                                            int32_t* __restrict__ counts) {
+  __shared__ int32_t part[kGroupPrefixWaves][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const int cw = (W + kGroupPrefixWaves - 1) / kGroupPrefixWaves;
+  const int w0 = min(wv * cw, W), w1 = min(w0 + cw, W);
+  int s = 0;
+  if (e < E)
+    for (int w = w0; w < w1; ++w) s += __popc(bm[int64_t(w) * E + e]);
+  part[wv][lane] = s;
+  __syncthreads();
+  int run = 0, tot = 0;
+  for (int v = 0; v < kGroupPrefixWaves; ++v) {
+    const int c = part[v][lane];
+    if (v < wv) run += c;
+    tot += c;
+  }
+  if (e >= E) return;
+  if (wv == 0) counts[e] = tot;
+  for (int w = w0; w < w1; ++w) {
+    pre[int64_t(w) * E + e] = run;
+    run += __popc(bm[int64_t(w) * E + e]);
+  }
+}
+
+// Step 3: every workgroup scans the expert counts itself (workgroup 0 also
+// writes offsets, active list and totals), then one thread per entry ranks
+// it in O(1): pre[w][e] + the popcount of the earlier tokens of its word.
+__global__ __launch_bounds__(256) void group_rank_kernel(
+    const int32_t* __restrict__ idx, int T, int k, int E, const uint32_t* __restrict__ bm,
+    const int32_t* __restrict__ pre, const int32_t* __restrict__ cnt,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ pos,
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active, int tpt,
+    int4* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
+  __shared__ int32_t s_off[kGroupMaxE + 1];
+  __shared__ int32_t s_act[kGroupMaxE + 1];
+  __shared__ int32_t s_tile[kGroupMaxE + 1];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) s_off[e] = cnt[e];
+  __syncthreads();
+  // the counts themselves were written by the previous kernel
+  group_scan_experts(E, tiles ? tpt : 1, s_off, s_act, s_tile, blockIdx.x == 0, nullptr, offsets,
+                     active, n_active, tiles ? n_tiles : nullptr);
+  __syncthreads();
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= T * k) return;
+  const int e = idx[j];
+  if (unsigned(e) >= unsigned(E)) {
+    pos[j] = -1;
+    return;
+  }
+  const int t = j / k;
+  const int64_t wi = int64_t(t >> 5) * E + e;
+  const int rank = pre[wi] + __popc(bm[wi] & ((1u << (t & 31)) - 1u));
+  group_place(j, e, rank, s_off, s_act, s_tile, tpt, perm, pos, tiles);
+}
+
+size_t group_scratch_words(int64_t T, int32_t E) {
+  const int64_t W = (T + 31) / 32;
+  return size_t(W * E * (T > kGroupSmallT ? 2 : 1));
+}
+
+hipError_t launch_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, uint32_t* scratch,
                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
                         int32_t* active, int32_t* n_active, int tpt, int4* tiles,
                         int32_t* n_tiles, hipStream_t stream) {
   if (tiles && tpt <= 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, stream, idx, int(T), k, E, bitmap,
-                     counts, offsets, perm, pos, active, n_active, tpt, tiles, n_tiles);
+  if (E <= 0 || E > kGroupMaxE || T < 0) return hipErrorInvalidValue;
+  if (T <= kGroupSmallT) {
+    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, stream, idx, int(T), k, E, scratch,
+                       counts, offsets, perm, pos, active, n_active, tpt, tiles, n_tiles);
+    return hipGetLastError();
+  }
+  const int W = int((T + 31) / 32);
+  uint32_t* bm = scratch;
+  int32_t* pre = reinterpret_cast<int32_t*>(scratch + int64_t(W) * E);
+  hipLaunchKernelGGL(group_bits_kernel, dim3(W), dim3(256), 0, stream, idx, int(T), k, E, bm);
+  hipLaunchKernelGGL(group_prefix_kernel, dim3((E + 63) / 64), dim3(64 * kGroupPrefixWaves), 0,
+                     stream, bm, W, E, pre, counts);
+  const int64_t nent = T * k;
+  hipLaunchKernelGGL(group_rank_kernel, dim3(unsigned((nent + 255) / 256)), dim3(256), 0, stream,
+                     idx, int(T), k, E, bm, pre, counts, offsets, perm, pos, active, n_active, tpt,
+                     tiles, n_tiles);
   return hipGetLastError();
 }
 

@@ -26,6 +26,7 @@ LAYOUT_VERSION = 1
 
 EXPORTS = ["dsq_status_string", "dsq_packed_bytes", "dsq_qweight_init", "dsq_pack_weights",
            "dsq_gemv", "dsq_gemm_workspace_bytes", "dsq_gemm", "dsq_moe_route_topk",
+           "dsq_moe_group_workspace_bytes", "dsq_moe_group",
            "dsq_moe_workspace_bytes", "dsq_moe_ffn", "dsq_topk_workspace_bytes", "dsq_topk",
            "dsq_gemv_topk", "dsq_moe_block_workspace_bytes", "dsq_moe_block",
            "dsq_expert_cache_init", "dsq_expert_cache_plan", "dsq_moe_cached_workspace_bytes",
@@ -84,6 +85,10 @@ def lib():
         L.dsq_gemm.restype = i32
         L.dsq_moe_route_topk.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
         L.dsq_moe_route_topk.restype = i32
+        L.dsq_moe_group_workspace_bytes.argtypes = [i64, i32, i32]
+        L.dsq_moe_group_workspace_bytes.restype = sz
+        L.dsq_moe_group.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.dsq_moe_group.restype = i32
         L.dsq_moe_workspace_bytes.argtypes = [i64, i32, i32, i64, i64, i32]
         L.dsq_moe_workspace_bytes.restype = sz
         L.dsq_moe_ffn.argtypes = [vp, vp, vp, pd, pd, pd, i64, i32, i32, vp, vp, sz, vp, vp, vp,
@@ -268,6 +273,27 @@ def moe_route_topk(logits: torch.Tensor, top_k: int, bias: torch.Tensor | None =
     _check(lib().dsq_moe_route_topk(_ptr(logits), _ptr(bias), T, E, top_k, _ptr(idx),
                                     _ptr(weights), _stream(stream)), "dsq_moe_route_topk")
     return idx, weights
+
+
+def moe_group_workspace_bytes(T: int, E: int, top_k: int) -> int:
+    return int(lib().dsq_moe_group_workspace_bytes(T, E, top_k))
+
+
+def moe_group(idx: torch.Tensor, E: int, workspace=None, stream=None):
+    """Stable grouping of the routing entries idx [T][top_k] by expert:
+    returns (counts [E], offsets [E+1], perm [T*k], pos [T*k]), int32."""
+    _need(idx, torch.int32, "idx")
+    T, k = idx.shape
+    dev = idx.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    pos = torch.empty(max(T * k, 1), dtype=torch.int32, device=dev)
+    wptr, wbytes = _workspace(workspace, moe_group_workspace_bytes(T, E, k), dev)
+    _check(lib().dsq_moe_group(_ptr(idx) if T else None, T, E, k, _ptr(counts), _ptr(offsets),
+                               _ptr(perm), _ptr(pos), wptr, wbytes, _stream(stream)),
+           "dsq_moe_group")
+    return counts, offsets, perm[:T * k], pos[:T * k]
 
 
 def moe_workspace_bytes(T: int, E: int, top_k: int, H: int, I: int, math: int) -> int:

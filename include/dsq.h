@@ -169,7 +169,12 @@ dsq_status dsq_gemv(const dsq_qweight* W, int64_t expert, const float* x, float*
 
 /*
  * dsq_gemm -- Y = X dequant(W[expert])^T for M activation rows (batched
- * decode and prefill).
+ * decode and prefill): the matmul of "Hand-writing a DeepSeek inference
+ * engine in pure C" (hnwysp.cn/news/134870) §3.3 with the dequantization
+ * (q - zero_point) * scale of §3.2 fused into its inner loop; many rows at
+ * once are the batched prompt processing that "Running a 284B-parameter LLM
+ * from 3.2 GB of RAM in plain C" (feinterview.poetries.top) names as the
+ * missing piece (one weight read reused by every prompt token).
  *   X : fp32 [M][K] device.   Y : fp32 [M][N] device (written).
  *   math : DSQ_MATH_FP32, DSQ_MATH_BF16_MFMA or DSQ_MATH_AUTO.
  *   workspace : device scratch of dsq_gemm_workspace_bytes(M, N, K, math)
@@ -180,8 +185,12 @@ dsq_status dsq_gemv(const dsq_qweight* W, int64_t expert, const float* x, float*
  *               FP32: X split into two bf16 parts in matrix-core operand
  *               order.
  * FP32: |err| <= 1e-5 * sum|x w| per output (M = 1 runs the GEMV; M >= 2
- * multiplies exact integer codes by x = hi + lo, |x - hi - lo| <= 2^-18 |x|,
- * on the matrix cores and applies zero point and scale per group in fp32).
+ * multiplies exact integer codes by x = hi + lo, |x - hi - lo| <= 2^-17 |x|,
+ * on the matrix cores and applies zero point and scale per group in fp32:
+ * the split leaves at most 2^-17 = 7.6e-6 of sum|x w|, the fp32 group sums
+ * and scaling the rest of the 1e-5; worst-case inputs -- every activation at
+ * the significand that maximises the split residual, every product of one
+ * sign -- are among the tests).
  * BF16_MFMA: X and the dequantized weights are rounded to bf16 and products
  * are summed in fp32: |err| <= 1e-2 * sum|x w| per output.
  * A workspace query of 0 for M >= 2 (or for BF16_MFMA) means the shape is
@@ -207,6 +216,37 @@ dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float*
  */
 dsq_status dsq_moe_route_topk(const float* logits, const float* bias, int64_t T, int32_t E,
                               int32_t top_k, int32_t* idx, float* weights, void* stream);
+
+/*
+ * dsq_moe_group -- group the T*top_k routing entries by expert
+ * ("Hand-writing a DeepSeek inference engine in pure C",
+ * hnwysp.cn/news/134870, §3.5: the tokens routed to one expert are gathered
+ * so that the expert's weights are read once).  A stable counting sort,
+ * integer only, so the result is exact:
+ *   counts[e]  = number of entries j = t*top_k + i with idx[j] == e
+ *   offsets[e] = counts[0] + ... + counts[e-1];  offsets[E] = their total
+ *   perm[p]    = the entries j in ascending (expert, j) order
+ *   pos[j]     = the p with perm[p] == j
+ *   idx       : int32 [T][top_k] device; the experts of one token are
+ *               distinct (as dsq_moe_route_topk returns them).  An entry
+ *               outside [0, E) is grouped nowhere (pos = -1); a repeated
+ *               expert within a token gives unspecified values, every
+ *               write still inside the outputs.
+ *   counts    : int32 [E];  offsets : int32 [E+1];  perm, pos : int32
+ *               [T*top_k] (perm's first offsets[E] entries written); device.
+ *   workspace : dsq_moe_group_workspace_bytes(T, E, top_k) bytes, 256-byte
+ *               aligned (contents on entry ignored).
+ * These are the grouping kernels dsq_moe_ffn runs.  Up to 256 tokens one
+ * workgroup does the work; beyond, every entry is ranked in O(1) from
+ * per-expert prefixes of bitmap popcounts.
+ * Limits: T <= 65536, 1 <= E <= 4096, 1 <= top_k <= min(E, 32).
+ * Errors: DSQ_ERR_INVALID_ARG (NULL), DSQ_ERR_SHAPE, DSQ_ERR_UNSUPPORTED,
+ * DSQ_ERR_ALIGN, DSQ_ERR_WORKSPACE, DSQ_ERR_NO_DEVICE, DSQ_ERR_HIP.
+ */
+size_t dsq_moe_group_workspace_bytes(int64_t T, int32_t E, int32_t top_k);
+dsq_status dsq_moe_group(const int32_t* idx, int64_t T, int32_t E, int32_t top_k,
+                         int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* pos,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * dsq_topk -- output-head selection: the k largest logits, which choose the
@@ -246,7 +286,13 @@ dsq_status dsq_gemv_topk(const dsq_qweight* W, int64_t expert, const float* x, f
                          size_t workspace_bytes, void* stream);
 
 /*
- * dsq_moe_ffn -- one routed MoE layer:
+ * dsq_moe_ffn -- one routed MoE layer ("Hand-writing a DeepSeek inference
+ * engine in pure C", hnwysp.cn/news/134870, §3.5: the router is a linear
+ * layer followed by softmax and top-k; the tokens routed to one expert are
+ * grouped so that its weights are read once; the expert outputs are summed
+ * with the routing weights; §3.4: softmax with the maximum subtracted; §3.2:
+ * the experts' weights dequantized inside the matmuls; the SwiGLU expert form
+ * and the renormalised weights are the workload's definition):
  *   l = X Wr^T (+ bias)                    router logits, fp32
  *   (idx, w) = route_topk(l)               as dsq_moe_route_topk
  *   group the T*top_k entries by expert    stable, ascending token order

@@ -40,13 +40,25 @@ FLAG_DEGENERATE = 1
 FLAG_NONFINITE = 2
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.c into liboracle.so with gcc (no GPU code involved)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+# AddressSanitizer + UndefinedBehaviorSanitizer build of the same source (a
+# host-only library; gcc, no GPU code): every out-of-bounds access, leak-free
+# misuse of malloc'd scratch or undefined operation aborts the process.
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+            "-g"]
+
+
+def build(force: bool = True, out: str = None, sanitize: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no GPU code involved).
+    With sanitize=True the library is instrumented with ASan/UBSan and
+    written to `out` (it can only be loaded into a process whose main program
+    preloads the ASan runtime)."""
+    dst = out or _LIB
+    if force or not os.path.exists(dst):
+        tmp = dst + ".tmp"
+        flags = [*CFLAGS, *(SANITIZE if sanitize else [])]
+        subprocess.check_call(["gcc", *flags, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, dst)
+    return dst
 
 
 _lib = None
@@ -84,6 +96,10 @@ def lib():
         L.orc_sb4_quantize.restype = i64
         L.orc_sb4_dequant_f64.argtypes = [vp, i64, i64, vp]
         L.orc_sb4_dequant_f64.restype = i32
+        L.orc_silu_f64.argtypes = [ctypes.c_double]
+        L.orc_silu_f64.restype = ctypes.c_double
+        L.orc_dsilu_f64.argtypes = [ctypes.c_double]
+        L.orc_dsilu_f64.restype = ctypes.c_double
         L.orc_expert_f64.argtypes = [vp, i64, i64] + [vp] * 9 + [i32, i32] + [vp] * 6
         L.orc_moe_f32.argtypes = ([vp, i64, i64, i64, i32, i32, vp, vp] + [vp] * 9
                                   + [i32, i32, i32, vp, vp, vp])
@@ -95,6 +111,16 @@ def lib():
 def _p(a: np.ndarray):
     assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
     return ctypes.c_void_p(a.ctypes.data)
+
+
+def silu(z: float) -> float:
+    """The oracle's silu(z) = z / (1 + e^-z) in fp64 (used by orc_expert_f64)."""
+    return float(lib().orc_silu_f64(float(z)))
+
+
+def dsilu(z: float) -> float:
+    """The oracle's d/dz silu(z) in fp64 (the tolerance helper of orc_expert_f64)."""
+    return float(lib().orc_dsilu_f64(float(z)))
 
 
 def set_threads(n: int) -> None:

@@ -243,3 +243,30 @@ def test_topk_validation_and_workspace_query():
     assert L.dsq_gemv_topk(ctypes.byref(d), 0, fake, fake, 101, fake, fake, ws, 1 << 20, None) == -2
     assert L.dsq_gemv_topk(ctypes.byref(d), 1, fake, fake, 1, fake, fake, ws, 1 << 20, None) == -1
     assert L.dsq_gemv_topk(ctypes.byref(d), 0, mis, fake, 1, fake, fake, ws, 1 << 20, None) == -3
+
+
+def test_moe_group_validation_and_workspace_query():
+    L = dsq.lib()
+    fake = ctypes.c_void_p(0x50000)
+    mis = ctypes.c_void_p(0x50002)
+    need = dsq.moe_group_workspace_bytes(100, 256, 6)
+    # bitmap (4 words x 256 experts), active list, count
+    assert need == 256 * 16 + 256 * 4 + 256
+    # many tokens: the per-expert prefixes double the bitmap
+    assert dsq.moe_group_workspace_bytes(4096, 256, 6) == 2 * 128 * 256 * 4 + 256 * 4 + 256
+    assert dsq.moe_group_workspace_bytes(65537, 256, 6) == 0
+    assert dsq.moe_group_workspace_bytes(4, 4097, 6) == 0
+    assert dsq.moe_group_workspace_bytes(4, 8, 9) == 0
+    grp = L.dsq_moe_group
+    assert grp(None, 4, 8, 2, fake, fake, fake, fake, fake, need, None) == -1
+    assert grp(fake, 4, 8, 2, None, fake, fake, fake, fake, need, None) == -1
+    assert grp(fake, 4, 8, 9, fake, fake, fake, fake, fake, need, None) == -2
+    assert grp(fake, -1, 8, 2, fake, fake, fake, fake, fake, need, None) == -2
+    assert grp(fake, 4, 5000, 2, fake, fake, fake, fake, fake, need, None) == -5
+    assert grp(fake, 4, 8, 40, fake, fake, fake, fake, fake, need, None) == -2
+    assert grp(fake, 70000, 8, 2, fake, fake, fake, fake, fake, need, None) == -5
+    assert grp(mis, 4, 8, 2, fake, fake, fake, fake, fake, need, None) == -3
+    w4 = dsq.moe_group_workspace_bytes(4, 8, 2)
+    assert grp(fake, 4, 8, 2, fake, fake, fake, fake, fake, w4 - 1, None) == -4
+    assert grp(fake, 4, 8, 2, fake, fake, fake, fake, None, w4, None) == -4
+    assert grp(fake, 4, 8, 2, fake, fake, fake, fake, mis, w4, None) == -3

@@ -11,10 +11,10 @@ Method: "Hand-writing a DeepSeek inference engine in pure C"
            GPU's set must be one of the sets the oracle admits within that
            bound; slots ordered by the kernel's own fp32 scores;
   w      : first-order softmax propagation of the logit bound, + 1e-6;
-  Y      : rel * sum_i w_i (S_i + P_i) + sum_i dw_i |y_i|, with S_i the
-           down-projection magnitude sum, P_i the first-order effect of a
-           relative error rel in the gate/up sums (both from the oracle), dw_i
-           the weight bound; rel = 1e-5 (fp32) or 1e-2 (bf16 MFMA).
+  Y      : rel * S_Y + sum_i dw_i |y_i|, S_Y = sum_i w_i S_i with S_i the
+           magnitude sum of expert i's down projection (fp64, from the
+           oracle), dw_i the weight bound; rel = 1e-5 (fp32) or 1e-2 (bf16
+           MFMA, plus a normwise relative error of at most 1e-2).
 """
 import numpy as np
 import pytest
@@ -114,10 +114,11 @@ def test_moe_batched_decode_32_tokens_skewed_full_size():
         f"max tokens per expert: {np.bincount(idx.reshape(-1)).max()}")
 
 
-def test_moe_prefill_256_tokens_full_size_sampled():
-    """256 tokens, 256 INT8 group-128 SwiGLU experts, bf16 MFMA path; routing
-    of all tokens is checked, the output on 8 sampled tokens."""
+def test_moe_prefill_256_tokens_full_size():
+    """256 tokens, 256 INT8 group-128 SwiGLU experts, bf16 MFMA path; the
+    routing and the output of every token are checked (so every (expert,
+    token tile) item of the grouped GEMMs is compared)."""
     say("moe prefill T=256 full size INT8 g128 bf16")
     fx = MoeFixture(256, 4096, 2048, 8, 128, seed=0)
     X = synth.normal((256, 4096), 1.0, 0, synth.X, 5, device="cuda")
-    check_moe(fx, X, 6, dsq.MATH_BF16_MFMA, 1e-2, tokens=[0, 1, 37, 100, 128, 200, 254, 255])
+    check_moe(fx, X, 6, dsq.MATH_BF16_MFMA, 1e-2)

@@ -166,6 +166,7 @@ def test_gemv_vocab_projection_full_size_sampled(bits, group):
     # the packed codes of those rows are the oracle's
     q, s, z = device_entry(qw)
     np.testing.assert_array_equal(q[rows], m.q)
-    np.testing.assert_array_equal(s[rows], m.scale)
+    np.testing.assert_array_equal(s[rows].view(np.uint32), m.scale.view(np.uint32))
+    np.testing.assert_array_equal(z[rows].view(np.uint32), m.zp.view(np.uint32))
     del w, qw
     torch.cuda.empty_cache()
