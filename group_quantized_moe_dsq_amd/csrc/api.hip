@@ -9,10 +9,18 @@
 #include <float.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "internal.h"
 
 using namespace dsq;
+
+// Scratch of dsq_moe_ffn_noalloc: one fixed array per device, loaded with
+// the library's code object (so no allocation at call time).  In host code
+// `scratch` names a host-side stand-in, never the device address: the
+// device address comes from hipGetSymbolAddress, taken once per device.
+static __device__ __align__(256) uint8_t scratch[DSQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -503,6 +511,58 @@ dsq_status dsq_moe_ffn(const float* X, const float* router_w, const float* bias,
   if ((s = check_device()) != DSQ_OK) return s;
   return run_moe(X, nullptr, 0.0f, nullptr, nullptr, router_w, bias, *gate, *up, *down, T, top_k,
                  use_bf16(math, T), Y, workspace, logits_out, idx_out, w_out, expert_counts_out,
+                 nullptr, nullptr, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept for the process.
+dsq_status noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int d = -1;
+  const hipError_t e = hipGetDevice(&d);
+  if (e != hipSuccess) return DSQ_ERR_NO_DEVICE;
+  if (d < 0 || d >= kMaxDevices) return DSQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[d]) {
+    void* p = nullptr;
+    const hipError_t g = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (g != hipSuccess || !p) return DSQ_ERR_HIP;
+    addr[d] = p;
+  }
+  *out = addr[d];
+  return DSQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsq_status dsq_moe_ffn_noalloc(const float* X, const float* router_w, const float* bias,
+                               const dsq_qweight* gate, const dsq_qweight* up,
+                               const dsq_qweight* down, int64_t T, int32_t top_k, int32_t math,
+                               float* Y, float* logits_out, int32_t* idx_out, float* w_out,
+                               int32_t* expert_counts_out, void* stream) {
+  dsq_status s = check_moe(X, router_w, bias, gate, up, down, T, top_k, math, Y, logits_out,
+                           idx_out, w_out, expert_counts_out);
+  if (s != DSQ_OK) return s;
+  const size_t need =
+      dsq_moe_workspace_bytes(T, int32_t(gate->batch), top_k, gate->K, gate->N, math);
+  if (need == 0) return DSQ_ERR_OVERFLOW;
+  if (need > size_t(DSQ_NOALLOC_SCRATCH_BYTES)) return DSQ_ERR_WORKSPACE;
+  if (T == 0) return DSQ_OK;
+  if ((s = check_device()) != DSQ_OK) return s;
+  void* ws = nullptr;
+  if ((s = noalloc_scratch(&ws)) != DSQ_OK) return s;
+  // the MoE kernels overwrite every scratch word they read, so the previous
+  // call's contents need no clearing
+  return run_moe(X, nullptr, 0.0f, nullptr, nullptr, router_w, bias, *gate, *up, *down, T, top_k,
+                 use_bf16(math, T), Y, ws, logits_out, idx_out, w_out, expert_counts_out,
                  nullptr, nullptr, (hipStream_t)stream);
 }
 

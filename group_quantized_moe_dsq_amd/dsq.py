@@ -27,7 +27,8 @@ LAYOUT_VERSION = 1
 EXPORTS = ["dsq_status_string", "dsq_packed_bytes", "dsq_qweight_init", "dsq_pack_weights",
            "dsq_gemv", "dsq_gemm_workspace_bytes", "dsq_gemm", "dsq_moe_route_topk",
            "dsq_moe_group_workspace_bytes", "dsq_moe_group",
-           "dsq_moe_workspace_bytes", "dsq_moe_ffn", "dsq_topk_workspace_bytes", "dsq_topk",
+           "dsq_moe_workspace_bytes", "dsq_moe_ffn", "dsq_moe_ffn_noalloc",
+           "dsq_topk_workspace_bytes", "dsq_topk",
            "dsq_gemv_topk", "dsq_moe_block_workspace_bytes", "dsq_moe_block",
            "dsq_expert_cache_init", "dsq_expert_cache_plan", "dsq_moe_cached_workspace_bytes",
            "dsq_moe_ffn_cached"]
@@ -94,6 +95,9 @@ def lib():
         L.dsq_moe_ffn.argtypes = [vp, vp, vp, pd, pd, pd, i64, i32, i32, vp, vp, sz, vp, vp, vp,
                                   vp, vp]
         L.dsq_moe_ffn.restype = i32
+        L.dsq_moe_ffn_noalloc.argtypes = [vp, vp, vp, pd, pd, pd, i64, i32, i32, vp, vp, vp, vp,
+                                          vp, vp]
+        L.dsq_moe_ffn_noalloc.restype = i32
         L.dsq_moe_block_workspace_bytes.argtypes = [i64, i32, i32, i64, i64, i32]
         L.dsq_moe_block_workspace_bytes.restype = sz
         L.dsq_moe_block.argtypes = [vp, vp, ctypes.c_float, vp, vp, pd, pd, pd, i64, i32, i32, vp,
@@ -327,6 +331,25 @@ def moe_ffn(layer: MoeLayer, X: torch.Tensor, math: int = MATH_AUTO, Y=None,
                              ctypes.c_void_p(workspace.data_ptr() + off),
                              workspace.numel() - off, _ptr(logits_out), _ptr(idx_out),
                              _ptr(w_out), _ptr(counts_out), _stream(stream)), "dsq_moe_ffn")
+    return Y
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+
+
+def moe_ffn_noalloc(layer: MoeLayer, X: torch.Tensor, math: int = MATH_AUTO, Y=None,
+                    logits_out=None, idx_out=None, w_out=None, counts_out=None, stream=None):
+    """dsq_moe_ffn_noalloc: the MoE layer on the library's fixed scratch (no
+    workspace argument; calls that overlap on one device race)."""
+    _need(X, torch.float32, "X")
+    T = X.shape[0]
+    if Y is None:
+        Y = torch.empty((T, layer.H), dtype=torch.float32, device=X.device)
+    _check(lib().dsq_moe_ffn_noalloc(_ptr(X), _ptr(layer.router_w), _ptr(layer.bias),
+                                     ctypes.byref(layer.gate.desc), ctypes.byref(layer.up.desc),
+                                     ctypes.byref(layer.down.desc), T, layer.top_k, math,
+                                     _ptr(Y), _ptr(logits_out), _ptr(idx_out), _ptr(w_out),
+                                     _ptr(counts_out), _stream(stream)), "dsq_moe_ffn_noalloc")
     return Y
 
 

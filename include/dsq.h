@@ -325,6 +325,31 @@ dsq_status dsq_moe_ffn(const float* X, const float* router_w, const float* bias,
                        float* w_out, int32_t* expert_counts_out, void* stream);
 
 /*
+ * dsq_moe_ffn_noalloc -- dsq_moe_ffn for callers that cannot allocate or pass
+ * device memory of their own: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  The same kernels and results as
+ * dsq_moe_ffn (bitwise), with the workspace taken from a fixed scratch array
+ * of DSQ_NOALLOC_SCRATCH_BYTES that the library's code object holds on every
+ * device it runs on, until the process ends.  The call allocates nothing.
+ *   Arguments as dsq_moe_ffn without workspace / workspace_bytes.
+ *   Limit: dsq_moe_workspace_bytes(T, E, top_k, H, I, math) <=
+ *   DSQ_NOALLOC_SCRATCH_BYTES (64 MiB: up to 64 tokens of the 4096-hidden,
+ *   2048-intermediate, 256-expert top-6 layer); larger calls return
+ *   DSQ_ERR_WORKSPACE and enqueue nothing.
+ *   Every call on a device shares that device's scratch: calls that may
+ *   overlap on one device (several streams, several host threads) race and
+ *   must be ordered by the caller.  The scratch keeps the last call's
+ *   contents; the kernels read none of it before writing it.
+ * Errors as dsq_moe_ffn, plus DSQ_ERR_WORKSPACE for sizes beyond the scratch.
+ */
+#define DSQ_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+dsq_status dsq_moe_ffn_noalloc(const float* X, const float* router_w, const float* bias,
+                               const dsq_qweight* gate, const dsq_qweight* up,
+                               const dsq_qweight* down, int64_t T, int32_t top_k, int32_t math,
+                               float* Y, float* logits_out, int32_t* idx_out, float* w_out,
+                               int32_t* expert_counts_out, void* stream);
+
+/*
  * dsq_moe_block -- the MoE step of a transformer block with its norm and
  * residual ("Hand-writing a DeepSeek inference engine in pure C",
  * hnwysp.cn/news/134870, §2.1: each block normalises with RMSNorm before the
