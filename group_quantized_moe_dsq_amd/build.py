@@ -51,19 +51,26 @@ def _run(cmd, verbose):
     return r
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    os.makedirs(OBJ, exist_ok=True)
-    objs = [os.path.join(OBJ, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    cmds = [[HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, s), "-o", o]
+def build(verbose: bool = False, extra=(), out: str = None, objdir: str = None,
+          csrc: str = None) -> str:
+    """Compile every source and link the library (to `out`, default the
+    in-tree libdsq.so); `extra` adds compiler flags (e.g. -D overrides of
+    the launch-shape macros)."""
+    obj = objdir or OBJ
+    os.makedirs(obj, exist_ok=True)
+    objs = [os.path.join(obj, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    src = csrc or CSRC
+    cmds = [[HIPCC, *FLAGS, *extra, "-c", os.path.join(src, s), "-o", o]
             for s, o in zip(SOURCES, objs)]
     workers = max(1, min(len(cmds), os.cpu_count() or 1, 16))
     with cf.ThreadPoolExecutor(workers) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB + ".tmp"
+    dst = out or LIB
+    tmp = dst + ".tmp"
     _run([HIPCC, *LINK, *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, dst)
+    return dst
 
 
 if __name__ == "__main__":
