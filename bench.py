@@ -119,6 +119,10 @@ def main():
                                        "gemm256,moe256",
                     help="secondary workloads to run (comma list)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default="",
+                    help="run just these secondary workloads (comma list, names as in "
+                         "--cases) and print their records: the command the per-kernel "
+                         "profiles are taken with")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of 1 GiB a few times: the reference "
                          "kernel of known traffic for scaling the FETCH_SIZE / WRITE_SIZE "
@@ -126,7 +130,13 @@ def main():
     ap.add_argument("--cpu-reps", type=int, default=5,
                     help="timed passes of the CPU baseline (median reported)")
     ap.add_argument("--cpu-child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--pmc-summary", nargs="+", metavar="CSV",
+                    help="print the per-kernel mean of every counter in rocprofv3 --pmc "
+                         "CSV files (library kernels only) and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
+        return
     if args.cpu_child:
         cpu_baseline_child(args.cpu_reps)
         return
@@ -143,6 +153,11 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only:
+        x = synth.normal((N_EMBD,), 1.0, 0, synth.X, 21, device=dev)
+        recs = secondary(dsq, synth, torch, np, dev, set(args.only.split(",")), x)
+        print(json.dumps({"only": args.only, "records": recs}), flush=True)
+        return
     if args.calibrate_copy:
         n = 1 << 28  # fp32 elements: 1 GiB read and 1 GiB written per copy
         a = torch.ones(n, device=dev)
@@ -447,6 +462,35 @@ def dense_prefill(dsq, synth, torch, dev):
     torch.cuda.empty_cache()
     return rec
 
+
+
+def pmc_summary(paths):
+    """Mean of each counter per dispatch of each library kernel, from the
+    per-dispatch rows rocprofv3 --pmc writes (*_counter_collection.csv); the
+    runtime's buffer copy is kept too, as the reference of known traffic."""
+    import collections
+    import csv
+    import re
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    info = {}
+    for path in paths:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                if "dsq::" not in name and "copyBuffer" not in name:
+                    continue
+                name = re.sub(r"\(dsq::.*|\(float const.*|\(.*", "", name).replace("void ", "")
+                vals[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                info[name] = (r["Grid_Size"], r["Workgroup_Size"], r["VGPR_Count"],
+                              r.get("Accum_VGPR_Count", ""), r["LDS_Block_Size"])
+    for name in sorted(vals):
+        cs = vals[name]
+        n = max(len(v) for v in cs.values())
+        g, wg, vg, ag, lds = info[name]
+        print(f"{name}  dispatches={n} grid={g} wg={wg} vgpr={vg} agpr={ag} lds={lds}")
+        for c in sorted(cs):
+            v = cs[c]
+            print(f"    {c:28s} mean {sum(v) / len(v):.6g}")
 
 
 def cpu_topology():
