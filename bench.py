@@ -53,29 +53,72 @@ def qbytes(bits, group, K, N):
     return N * K * bits // 8 + N * (K // group) * (16 if group == 256 else 8)
 
 
-# the sources that define the dominant kernel (the fused-dequant GEMV)
-GEMV_SOURCES = ("gemv.hip", "gemv_core.h", "head_key.h", "common.h")
+RECORDS = os.path.join(ROOT, "profiles", "records.json")
+CSRC = os.path.join(ROOT, "group_quantized_moe_dsq_amd", "csrc")
 
 
-def kernel_source_hash():
+def library_source_hash():
+    """Hash of every kernel source: a profile record counts for the sources
+    it was taken on only."""
     h = hashlib.sha256()
-    for f in GEMV_SOURCES:
-        with open(os.path.join(ROOT, "group_quantized_moe_dsq_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def traffic_record():
-    """HBM bytes per launch of the dominant kernel measured with rocprofv3
-    counters (profiles/traffic_vocab_gemv.json), if taken on this source."""
-    p = os.path.join(ROOT, "profiles", "traffic_vocab_gemv.json")
-    if not os.path.exists(p):
+def load_records():
+    if not os.path.exists(RECORDS):
+        return {}
+    with open(RECORDS) as fh:
+        return json.load(fh)
+
+
+def kernel_record(workload, prefix):
+    """(name, record) of the kernel of workload's committed rocprofv3 profile
+    whose name starts with `prefix` and which took the most GPU time, with the
+    counter calibration (fetch scale, write scale); None when there is no
+    record for the current sources."""
+    recs = load_records()
+    w = recs.get("workloads", {}).get(workload)
+    cal = recs.get("calibration") or {}
+    if not w or w.get("source_hash") != library_source_hash():
         return None
-    with open(p) as fh:
-        rec = json.load(fh)
-    if rec.get("source_hash") != kernel_source_hash():
+    cands = [(k, v) for k, v in w.get("kernels", {}).items() if k.startswith(prefix)]
+    if not cands:
         return None
-    return rec.get("bytes_per_launch")
+    name, k = max(cands, key=lambda kv: kv[1].get("calls", 0) * kv[1].get("avg_us", 0.0))
+    return name, k, cal.get("fetch_scale"), cal.get("write_scale")
+
+
+def roofline_entry(workload, kernel, bound, work, unit_work, graph_us=None):
+    """Roofline of the workload's dominant kernel from its committed profile
+    record: achieved = algorithmic work per launch (bytes or flops) / the
+    kernel's average rocprof duration; traffic = FETCH_SIZE + WRITE_SIZE per
+    dispatch scaled by the plain-copy calibration.  Fields are null when no
+    record was taken on the current sources."""
+    peak = HBM_PEAK_GBS if bound == "hbm" else BF16_PEAK_TFLOPS
+    unit = "GB/s" if bound == "hbm" else "TFLOP/s"
+    e = {"kernel": kernel, "bound": bound, "peak": peak, "unit": unit,
+         unit_work: work, "kernel_us": None, "achieved": None, "frac": None, "traffic": None}
+    if graph_us is not None:
+        e["graph_us_per_call"] = graph_us
+    r = kernel_record(workload, kernel)
+    if r is None:
+        e["note"] = "no rocprofv3 record of this workload on the current sources"
+        return e
+    e["kernel"], k, fs, ws = r
+    us = k.get("avg_us")
+    if us:
+        e["kernel_us"] = us
+        scale = 1e9 if bound == "hbm" else 1e12
+        e["achieved"] = round(work / (us * 1e-6) / scale, 1)
+        e["frac"] = round(e["achieved"] / peak, 4)
+    if k.get("FETCH_SIZE") is not None and k.get("WRITE_SIZE") is not None and fs and ws:
+        e["traffic"] = int(k["FETCH_SIZE"] * 1024 * fs + k["WRITE_SIZE"] * 1024 * ws)
+    return e
 
 
 def time_calls(fn, iters, warmup, torch, graph=True, replays=5):
@@ -133,7 +176,17 @@ def main():
     ap.add_argument("--pmc-summary", nargs="+", metavar="CSV",
                     help="print the per-kernel mean of every counter in rocprofv3 --pmc "
                          "CSV files (library kernels only) and exit")
+    ap.add_argument("--record", metavar="WORKLOAD",
+                    help="store the library kernels' rocprofv3 figures of WORKLOAD (the "
+                         "--only name, or 'calibration' for --calibrate-copy) from --kt / --pmc "
+                         "CSV files into profiles/records.json, keyed to the current sources")
+    ap.add_argument("--kt", metavar="CSV", help="rocprofv3 --stats kernel statistics CSV")
+    ap.add_argument("--pmc", nargs="*", default=[], metavar="CSV",
+                    help="rocprofv3 --pmc counter collection CSVs")
     args = ap.parse_args()
+    if args.record:
+        store_record(args.record, args.kt, args.pmc)
+        return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary)
         return
@@ -155,7 +208,7 @@ def main():
     torch.cuda.set_device(dev)
     if args.only:
         x = synth.normal((N_EMBD,), 1.0, 0, synth.X, 21, device=dev)
-        recs = secondary(dsq, synth, torch, np, dev, set(args.only.split(",")), x)
+        recs = secondary(dsq, synth, torch, np, dev, set(args.only.split(",")), x, floor=False)
         print(json.dumps({"only": args.only, "records": recs}), flush=True)
         return
     if args.calibrate_copy:
@@ -213,7 +266,7 @@ def main():
     achieved = bytesv / (vocab_ms * 1e-3) / 1e9
     log(f"headline: {ms_per_step * 1e3:.1f} us/step, {value:.0f} GB/s; vocab gemv "
         f"{vocab_ms * 1e3:.1f} us = {achieved:.0f} GB/s")
-    traffic = traffic_record()
+    prof = roofline_entry("gemv8vocab", "dsq::gemv_kernel<8", "hbm", bytesv, "algorithmic_bytes")
 
     result = {
         "metric": "effective weight GB/s (% of HBM peak) for INT4/INT8 GEMV + MoE FFN; "
@@ -235,8 +288,14 @@ def main():
                    "step_bytes": step_bytes, "hbm_frac": round(value / HBM_PEAK_GBS, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "dsq::gemv_kernel<8, 2, 4> (INT8 g64 vocab GEMV 4096x129280)",
-                     "kernel_us": round(vocab_ms * 1e3, 2), "algorithmic_bytes": bytesv},
+                     "traffic": prof["traffic"],
+                     "kernel": (prof["kernel"] if prof["kernel_us"] else "dsq::gemv_kernel<8, ...>")
+                     + " (INT8 g64 vocab GEMV 4096x129280)",
+                     "kernel_us": round(vocab_ms * 1e3, 2), "algorithmic_bytes": bytesv,
+                     "timing": "HIP events on the launch stream around replays of a graph of 100 "
+                               "back-to-back launches",
+                     "kernel_us_rocprof": prof["kernel_us"],
+                     "frac_rocprof": prof["frac"]},
     }
     del W4
     torch.cuda.empty_cache()
@@ -268,11 +327,11 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def secondary(dsq, synth, torch, np, dev, cases, x):
+def secondary(dsq, synth, torch, np, dev, cases, x, floor=True):
     out = []
     K = 4096
 
-    def rotated_gemv(bits, group, name, copies):
+    def rotated_gemv(bits, group, name, copies, case, kname):
         Ws = []
         for c in range(copies):
             w = synth.normal((4096, K), 0.02, 0, synth.W, 100 + c, device=dev)
@@ -284,20 +343,36 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
         ms = time_calls(lambda i: dsq.gemv(Ws[i % copies], x, y), 400, 64, torch)
         b = qbytes(bits, group, K, 4096) + K * 4 + 4096 * 4
         gbs = b / (ms * 1e-3) / 1e9
-        out.append({"workload": name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
-                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-                    "note": f"rotating {copies} weight copies ({copies * b / 1e6:.0f} MB) "
-                            "so the Infinity Cache cannot hold them"})
+        rec = {"workload": name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+               "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+               "note": f"rotating {copies} weight copies ({copies * b / 1e6:.0f} MB) "
+                       "so the Infinity Cache cannot hold them"}
+        if floor:
+            # per-launch floor of back-to-back graph launches of this kernel:
+            # the same GEMV format on a 64x256 matrix (a few KB, cache
+            # resident); left out of the single-workload (profiled) runs so
+            # that the profile holds the 4096x4096 launches only
+            wt = synth.normal((64, 256), 0.02, 0, synth.W, 99, device=dev)
+            qt = dsq.QWeight(bits, group, 256, 64)
+            dsq.pack_weights(wt, qt)
+            xt = synth.normal((256,), 1.0, 0, synth.X, 99, device=dev)
+            yt = torch.empty(64, device=dev)
+            floor_ms = time_calls(lambda i: dsq.gemv(qt, xt, yt), 400, 64, torch)
+            rec["launch_floor_us"] = round(floor_ms * 1e3, 2)
+        rec["roofline"] = roofline_entry(case, kname, "hbm", b, "algorithmic_bytes",
+                                         graph_us=rec["us"])
+        out.append(rec)
         log(out[-1])
 
     if "gemv8" in cases:
-        rotated_gemv(8, 64, "INT8 g64 GEMV 4096x4096 (M=1)", 64)
+        rotated_gemv(8, 64, "INT8 g64 GEMV 4096x4096 (M=1)", 64, "gemv8", "dsq::gemv_kernel<8")
     if "gemv4" in cases:
-        rotated_gemv(4, 64, "INT4 g64 GEMV 4096x4096 (M=1)", 64)
+        rotated_gemv(4, 64, "INT4 g64 GEMV 4096x4096 (M=1)", 64, "gemv4", "dsq::gemv_kernel<4")
     if "sb4" in cases:
-        rotated_gemv(4, 256, "super-block 4-bit GEMV 4096x4096 (M=1)", 64)
+        rotated_gemv(4, 256, "super-block 4-bit GEMV 4096x4096 (M=1)", 64, "sb4",
+                     "dsq::gemv_sb4_kernel")
     torch.cuda.empty_cache()
-    def vocab_gemv(bits, group, name):
+    def vocab_gemv(bits, group, name, case, kname):
         # the vocab projection, 298-331 MB: cold by size
         NV = N_VOCAB
         w = synth.normal((NV, K), 0.02, 0, synth.W, 2, device=dev)
@@ -310,15 +385,20 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
         b = qbytes(bits, group, K, NV) + K * 4 + NV * 4
         gbs = b / (ms * 1e-3) / 1e9
         out.append({"workload": name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
-                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": b})
+                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": b,
+                    "roofline": roofline_entry(case, kname, "hbm", b, "algorithmic_bytes",
+                                               graph_us=round(ms * 1e3, 2))})
         log(out[-1])
         del q
         torch.cuda.empty_cache()
 
+    if "gemv8vocab" in cases:  # the headline's dominant kernel alone (for its profile)
+        vocab_gemv(8, 64, "INT8 g64 vocab GEMV 4096x129280 (M=1)", "gemv8vocab", "dsq::gemv_kernel<8")
     if "gemv4vocab" in cases:
-        vocab_gemv(4, 64, "INT4 g64 vocab GEMV 4096x129280 (M=1)")
+        vocab_gemv(4, 64, "INT4 g64 vocab GEMV 4096x129280 (M=1)", "gemv4vocab", "dsq::gemv_kernel<4")
     if "sb4vocab" in cases:
-        vocab_gemv(4, 256, "super-block 4-bit vocab GEMV 4096x129280 (M=1)")
+        vocab_gemv(4, 256, "super-block 4-bit vocab GEMV 4096x129280 (M=1)", "sb4vocab",
+                   "dsq::gemv_sb4_kernel")
 
     # MoE decode layers: 256 experts, H=4096, I=2048, top-6
     def build_moe(bits, group, bias_std):
@@ -336,7 +416,8 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
         torch.cuda.synchronize()
         return router, bias, g, u, d
 
-    def moe_case(name, layer, T, nsets, math, bits, group, iters, block=False):
+    def moe_case(name, layer, T, nsets, math, bits, group, iters, block=False, case=None,
+                 kernels=None):
         # block: the MoE step with its RMSNorm and residual (dsq_moe_block)
         H = N_EMBD
         Xs = [synth.normal((T, H), 1.0, 0, synth.X, 1000 + T * 100 + s, device=dev)
@@ -365,6 +446,19 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
         rec = {"workload": name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "experts_touched": D,
                "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 3)}
+        if case and kernels:
+            # the weight-streaming kernels: gate/up reads the touched experts'
+            # gate and up matrices, down their down matrices (codes + fp32
+            # scale and zero point); the dominant one is gate/up
+            gu_bytes = int(D * 2 * qbytes(bits, group, H, 2048))
+            dn_bytes = int(D * qbytes(bits, group, 2048, H))
+            rec["roofline"] = roofline_entry(case, kernels[0], "hbm", gu_bytes, "algorithmic_bytes")
+            rec["roofline_down"] = roofline_entry(case, kernels[1], "hbm", dn_bytes,
+                                                  "algorithmic_bytes")
+            w = load_records().get("workloads", {}).get(case)
+            if w and w.get("source_hash") == library_source_hash():
+                rec["kernels_us"] = {k: v.get("avg_us") for k, v in sorted(w["kernels"].items())
+                                     if not k.startswith("dsq::pack")}
         out.append(rec)
         log(rec)
 
@@ -372,7 +466,8 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
         r, b, g, u, d = build_moe(4, 64, None)
         if "moe1" in cases:
             moe_case("MoE decode T=1, 256 experts top-6, INT4 g64 SwiGLU",
-                     dsq.MoeLayer(r, g, u, d, None, N_EXPERT_USED), 1, 64, dsq.MATH_FP32, 4, 64, 64)
+                     dsq.MoeLayer(r, g, u, d, None, N_EXPERT_USED), 1, 64, dsq.MATH_FP32, 4, 64, 64,
+                     case="moe1", kernels=("dsq::dec_gateup_kernel", "dsq::dec_down_kernel"))
         if "block1" in cases:
             moe_case("MoE block decode T=1 (RMSNorm + MoE + residual), INT4 g64 SwiGLU",
                      dsq.MoeLayer(r, g, u, d, None, N_EXPERT_USED), 1, 64, dsq.MATH_FP32, 4, 64, 64,
@@ -382,7 +477,9 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
         if "moe32" in cases:
             bias = synth.normal((256,), 1.0, 0, synth.BIAS, 0, device=dev)
             moe_case("MoE batched decode T=32 skewed (router bias ~N(0,1)), INT4 g64",
-                     dsq.MoeLayer(r, g, u, d, bias, N_EXPERT_USED), 32, 8, dsq.MATH_FP32, 4, 64, 16)
+                     dsq.MoeLayer(r, g, u, d, bias, N_EXPERT_USED), 32, 8, dsq.MATH_FP32, 4, 64, 16,
+                     case="moe32", kernels=("dsq::gmm_kernel<4, 2, 2, true>",
+                                            "dsq::gmm_kernel<4, 2, 2, false>"))
         del g, u, d
         torch.cuda.empty_cache()
     if "gemm256" in cases:
@@ -390,7 +487,9 @@ def secondary(dsq, synth, torch, np, dev, cases, x):
     if "moe256" in cases:
         r, b, g, u, d = build_moe(8, 128, None)
         moe_case("MoE prefill T=256, 256 experts top-6, INT8 g128 SwiGLU, bf16 MFMA",
-                 dsq.MoeLayer(r, g, u, d, None, N_EXPERT_USED), 256, 1, dsq.MATH_BF16_MFMA, 8, 128, 8)
+                 dsq.MoeLayer(r, g, u, d, None, N_EXPERT_USED), 256, 1, dsq.MATH_BF16_MFMA, 8, 128, 8,
+                 case="moe256", kernels=("dsq::gmm_kernel<8, 4, 1, true>",
+                                         "dsq::gmm_kernel<8, 4, 1, false>"))
         del g, u, d
         torch.cuda.empty_cache()
     return out
@@ -456,12 +555,105 @@ def dense_prefill(dsq, synth, torch, dev):
     rec = {"workload": "dense prefill GEMM M=256 K=N=4096 INT8 g128 bf16 MFMA",
            "us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
            "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
-           "GB/s": round((qbytes(8, 128, K, 4096) + 2 * 256 * K * 4) / (ms * 1e-3) / 1e9, 1)}
+           "GB/s": round((qbytes(8, 128, K, 4096) + 2 * 256 * K * 4) / (ms * 1e-3) / 1e9, 1),
+           "roofline": roofline_entry("gemm256", "dsq::gemm_mfma_kernel", "mfma", flops,
+                                      "algorithmic_flops", graph_us=round(ms * 1e3, 2))}
+    w = load_records().get("workloads", {}).get("gemm256")
+    if w and w.get("source_hash") == library_source_hash():
+        rec["kernels_us"] = {k: v.get("avg_us") for k, v in sorted(w["kernels"].items())
+                             if not k.startswith("dsq::pack")}
     log(rec)
     del Ws
     torch.cuda.empty_cache()
     return rec
 
+
+
+def _kernel_name(raw):
+    """'void dsq::gmm_kernel<8, 4, 1, true>(dsq::GmmArgs)' -> 'dsq::gmm_kernel<8, 4, 1, true>'."""
+    import re
+    name = raw.replace("void ", "", 1) if raw.startswith("void ") else raw
+    m = re.match(r"^([^(]*?(?:<.*?>)?)\(", name)
+    return (m.group(1) if m else name).strip()
+
+
+def _pmc_means(paths):
+    import collections
+    import csv
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"]
+                if "dsq::" not in name and "copyBuffer" not in name:
+                    continue
+                vals[_kernel_name(name)][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in vals.items()}, \
+        {k: max(len(v) for v in cs.values()) for k, cs in vals.items()}
+
+
+def store_record(workload, kt, pmc):
+    """Merge one workload's rocprofv3 figures into profiles/records.json."""
+    import csv
+    recs = load_records()
+    means, counts = _pmc_means(pmc)
+    counters = sorted({c for m in means.values() for c in m})
+    if workload == "calibration":
+        copy = next((v for k, v in means.items() if "copyBuffer" in k), None)
+        if copy is None:
+            sys.exit("no buffer copy kernel in the counter files")
+        n = 1 << 30  # bytes read and written by the --calibrate-copy copy
+        cal = recs.get("calibration", {})
+        if "FETCH_SIZE" in copy:
+            cal["fetch_scale"] = round(n / 1024 / copy["FETCH_SIZE"], 5)
+            cal["FETCH_SIZE_KiB"] = copy["FETCH_SIZE"]
+        if "WRITE_SIZE" in copy:
+            cal["write_scale"] = round(n / 1024 / copy["WRITE_SIZE"], 5)
+            cal["WRITE_SIZE_KiB"] = copy["WRITE_SIZE"]
+        cal["reference"] = "device copy of 1 GiB fp32 (bench.py --calibrate-copy), bytes read " \
+                           "and written known"
+        cal["commands"] = sorted(set(cal.get("commands", [])) | {
+            f"rocprofv3 --pmc {c} --output-format csv -d <dir> -o r -- python3 -u bench.py "
+            "--calibrate-copy" for c in counters})
+        recs["calibration"] = cal
+    else:
+        w = recs.setdefault("workloads", {}).get(workload, {})
+        if w.get("source_hash") != library_source_hash():
+            w = {}
+        w["source_hash"] = library_source_hash()
+        kernels = w.setdefault("kernels", {})
+        cmds = set(w.get("commands", []))
+        if kt:
+            with open(kt) as fh:
+                for r in csv.DictReader(fh):
+                    if "dsq::" not in r["Name"]:
+                        continue
+                    k = kernels.setdefault(_kernel_name(r["Name"]), {})
+                    k["calls"] = int(r["Calls"])
+                    k["avg_us"] = round(float(r["AverageNs"]) / 1000, 3)
+                    k["min_us"] = round(float(r["MinNs"]) / 1000, 3)
+                    k["max_us"] = round(float(r["MaxNs"]) / 1000, 3)
+            cmds.add("rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o r -- "
+                     f"python3 -u bench.py --only {workload}")
+        for name, m in means.items():
+            if "copyBuffer" in name:
+                continue
+            k = kernels.setdefault(name, {})
+            k.update({c: round(v, 3) for c, v in m.items()})
+            k["dispatches_counted"] = counts[name]
+        for path in pmc:
+            with open(path) as fh:
+                import csv as _csv
+                names = sorted({r["Counter_Name"] for r in _csv.DictReader(fh)})
+            cmds.add(f"rocprofv3 --pmc {' '.join(names)} --output-format csv -d <dir> -o r -- "
+                     f"python3 -u bench.py --only {workload}")
+        w["commands"] = sorted(cmds)
+        recs["workloads"][workload] = w
+    os.makedirs(os.path.dirname(RECORDS), exist_ok=True)
+    with open(RECORDS, "w") as fh:
+        json.dump(recs, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(f"recorded {workload} into {RECORDS}")
 
 
 def pmc_summary(paths):
