@@ -736,6 +736,10 @@ def cpu_baseline_child(reps):
     import oracle
     from group_quantized_moe_dsq_amd import synth
 
+    # importing torch (through synth) resets the OpenMP thread count of the
+    # process; the parent's OMP_NUM_THREADS is applied again here
+    if os.environ.get("OMP_NUM_THREADS"):
+        oracle.set_threads(int(os.environ["OMP_NUM_THREADS"]))
     K, NV = N_EMBD, N_VOCAB
     # the same shapes, seeds and distributions as the GPU phase, drawn with
     # the CPU generator
