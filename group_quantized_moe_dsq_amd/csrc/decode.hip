@@ -370,9 +370,8 @@ __device__ __forceinline__ void dec_lane(DecLane<BITS, J, NT>& ln, const uint8_t
   }
 }
 
-template <int BITS, int J, int NT>
-__device__ __forceinline__ void dec_issue(const DecLane<BITS, J, NT>& ln, uint8_t* slot, int m,
-                                          int lane) {
+template <int BITS, int J, int NT, class Lane>
+__device__ __forceinline__ void dec_issue(const Lane& ln, uint8_t* slot, int m, int lane) {
   using R = DecRing<BITS, J, NT>;
 #pragma unroll
   for (int b = 0; b < NT; ++b)
@@ -382,41 +381,53 @@ __device__ __forceinline__ void dec_issue(const DecLane<BITS, J, NT>& ln, uint8_
                                                16, ln.vdc[b][h] + m * (kDecWaves * 128), 0, 0, 0);
   if (lane < 16 * R::PPR) {
 #pragma unroll
-    for (int b = 0; b < NT; ++b)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ln.rm[b],
-                                               (lds_ptr_t)(slot + R::CSLOT + b * 16 * R::L * 8),
-                                               R::PB, ln.vdm[b] + m * (kDecWaves * R::L * 8), 0, 0,
-                                               0);
+    for (int b = 0; b < NT; ++b) {
+      lds_ptr_t dst = (lds_ptr_t)(slot + R::CSLOT + b * 16 * R::L * 8);
+      const int off = ln.vdm[b] + m * (kDecWaves * R::L * 8);
+      // the piece size as a literal (the builtin takes a constant)
+      if constexpr (R::PB == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(ln.rm[b], dst, 16, off, 0, 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(ln.rm[b], dst, 4, off, 0, 0, 0);
+    }
   }
 }
 
 // Products of step m of the wave's share (groups s_lo + 8 L m .. + L, s_lo =
 // L w): for every group s of the step below s_hi, y[b] += the group's fp32
 // correction of the MFMA sum of the activation parts (rows 0, 1 of A) times
-// tile b's codes.
-template <int BITS, int J, int NT>
-__device__ __forceinline__ void dec_step(const uint8_t* slot, f32x4_t (&y)[NT], const uint16_t* xp,
-                                         const float4* xs, int K, int G, int s_lo, int s_hi,
-                                         int m, int lane, const uint32_t* zeros) {
+// tile b's codes.  SHARED: every tile takes the activation xp[0] / xs[0]
+// (gate and up of one slot); else tile b takes xp[b] / xs[b] (the tiles of
+// different slots).
+template <int BITS, int J, int NT, bool SHARED>
+__device__ __forceinline__ void dec_step(const uint8_t* slot, f32x4_t (&y)[NT],
+                                         const uint16_t* const (&xp)[NT],
+                                         const float4* const (&xs)[NT], int K, int G, int s_lo,
+                                         int s_hi, int m, int lane, const uint32_t* zeros) {
   using R = DecRing<BITS, J, NT>;
   constexpr float kOff = BITS == 4 ? 16.0f : 0.0f;
+  constexpr int NA = SHARED ? 1 : NT;  // activations read per group
   const int c = lane & 15, g4 = lane >> 4;
 #pragma unroll
   for (int sl = 0; sl < R::L; ++sl) {
     const int s = s_lo + m * (kDecWaves * R::L) + sl;
     if (s >= s_hi) break;  // uniform
-    u32x4_t af[J];
+    u32x4_t af[NA][J];
+    f32x2_t xv[NA];
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int k = s * G + g4 * 8 * J + 8 * j;
-      const uint16_t* a = c < 2 ? xp + int64_t(c) * K + k : reinterpret_cast<const uint16_t*>(zeros);
-      af[j] = *reinterpret_cast<const u32x4_t*>(a);
+    for (int a = 0; a < NA; ++a) {
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int k = s * G + g4 * 8 * J + 8 * j;
+        const uint16_t* src =
+            c < 2 ? xp[a] + int64_t(c) * K + k : reinterpret_cast<const uint16_t*>(zeros);
+        af[a][j] = *reinterpret_cast<const u32x4_t*>(src);
+      }
+      // the group's sums (hi, lo): read by every lane, used by lanes g4 = 0
+      xv[a] = lds_read_f32x2(xs[a] + s);
     }
-    // the group's sums (hi, lo): read by every lane, used by lanes g4 = 0
-    f32x2_t xv = lds_read_f32x2(xs + s);
     const int off = sl * (G * BITS / 8) + g4 * R::LB;  // byte of the 128-byte window
 #pragma unroll
     for (int b = 0; b < NT; ++b) {
+      const int a = SHARED ? 0 : b;
       const uint8_t* row = slot + b * 2048 + c * 128;
       uint32_t w[R::LB / 4];
       if constexpr (R::LB == 8) {
@@ -441,13 +452,16 @@ __device__ __forceinline__ void dec_step(const uint8_t* slot, f32x4_t (&y)[NT], 
         u32x4_t bq;
         if constexpr (BITS == 4) bq = int4_to_bf16(w[j]);
         else bq = int8_to_bf16(w[2 * j], w[2 * j + 1]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[j]),
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, af[a][j]),
                                                       __builtin_bit_cast(bf16x8_t, bq), acc, 0, 0,
                                                       0);
       }
       const float sc = mq[0], zq = mq[1] + kOff;
-      if (b == 0) lgkm_wait(xv);
-      const float x0 = g4 == 0 ? xv[0] : 0.0f, x1 = g4 == 0 ? xv[1] : 0.0f;
+      if (b == 0) {
+#pragma unroll
+        for (int q = 0; q < NA; ++q) lgkm_wait(xv[q]);
+      }
+      const float x0 = g4 == 0 ? xv[a][0] : 0.0f, x1 = g4 == 0 ? xv[a][1] : 0.0f;
       y[b][0] = fmaf(sc, fmaf(-zq, x0, acc[0]), y[b][0]);
       y[b][1] = fmaf(sc, fmaf(-zq, x1, acc[1]), y[b][1]);
     }
@@ -598,7 +612,10 @@ __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
     for (int m = 0; m < NS; ++m) {
       issue_next();  // into the slot computed in the previous iteration
       st.wait_oldest();
-      dec_step<BITS, J, 2>(st.slot(st.consumed), y, xp, xs, H, G, s_lo, s_hi, m, lane, zeros);
+      const uint16_t* const xpa[2] = {xp, xp};
+      const float4* const xsa[2] = {xs, xs};
+      dec_step<BITS, J, 2, true>(st.slot(st.consumed), y, xpa, xsa, H, G, s_lo, s_hi, m, lane,
+                                 zeros);
       ++st.consumed;
     }
     // rows 0 and 1 of the tile are the two parts of the token's product
@@ -615,14 +632,15 @@ __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
 // down + combine: Y[t][n] = sum_i w[t][i] (h[t*k+i] . Wd_{idx[t][i]}[n]).
 // Units (token t, 16-row tile of H) are dealt in a fixed stride; a workgroup
 // stages the token's k activation parts, wave w streams the pieces w, w + 8,
-// ... of I (L groups each) of each slot's tile in slot order, weights each slot's
-// partial sum by w[t][i], and the eight waves' sums meet in LDS in a fixed
+// ... of I (L groups each) of the slots' tiles, NT slots per step (NT = 2:
+// slots 2i and 2i + 1 together, the same rows of two experts, so a step
+// carries 4 KB of codes per wave), weights each slot's partial sum by
+// w[t][i] in slot order, and the eight waves' sums meet in LDS in a fixed
 // order.
 // ---------------------------------------------------------------------------
-template <int BITS, int J>
-__global__ __launch_bounds__(512) void dec_down_kernel(DecArgs p, int T) {
-  using R = DecRing<BITS, J, 1>;
-  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+template <int BITS, int J, int NT>
+__device__ __forceinline__ void dec_down_body(const DecArgs& p, int T, uint8_t* dsm) {
+  using R = DecRing<BITS, J, NT>;
   __shared__ float red[kDecWaves][16];
   __shared__ __attribute__((aligned(16))) uint32_t zeros[4];
   __shared__ int32_t s_rows[32];
@@ -655,26 +673,30 @@ __global__ __launch_bounds__(512) void dec_down_kernel(DecArgs p, int T) {
   auto unit_of = [&](int j) { return int(blockIdx.x) + j * int(gridDim.x); };
   if (unit_of(0) >= units) return;
 
-  DecStream<BITS, J, 1> st;
+  DecStream<BITS, J, NT> st;
   st.ring = rings + wv * R::BYTES;
-  // lookahead position (unit j, slot i, step m)
+  // lookahead position (unit j, slot group i of NT slots, step m)
   int lj = 0, li = 0, lm = 0;
-  DecLane<BITS, J, 1> ln;
+  const int kg = k / NT;  // slot groups (NT divides k)
+  DecLane<BITS, J, NT> ln;
   auto lane_for = [&](int j, int i) {
     const int u = unit_of(j);
     const int t = u / tiles;
-    const int e = s_e[t * k + i];
-    const uint8_t* const mat[1] = {p.down + int64_t(e) * p.d_stride};
-    dec_lane<BITS, J, 1>(ln, mat, p.d_meta_off, H, I, G, (u % tiles) * 16, s_lo, lane);
+    const uint8_t* mat[NT];
+#pragma unroll
+    for (int b = 0; b < NT; ++b) mat[b] = p.down + int64_t(s_e[t * k + NT * i + b]) * p.d_stride;
+    const uint8_t* const (&cmat)[NT] = mat;
+    dec_lane<BITS, J, NT>(ln, cmat, p.d_meta_off, H, I, G, (u % tiles) * 16, s_lo, lane);
   };
   lane_for(0, 0);
   auto issue_next = [&]() {
     if (unit_of(lj) >= units) return;
-    dec_issue<BITS, J, 1>(ln, st.slot(st.issued), lm, lane);
+    uint8_t* const sp = st.ring + (st.issued % R::DEPTH) * R::WSLOT;
+    dec_issue<BITS, J, NT>(ln, sp, lm, lane);
     ++st.issued;
     if (++lm == NS) {
       lm = 0;
-      if (++li == k) {
+      if (++li == kg) {
         li = 0;
         ++lj;
       }
@@ -698,16 +720,28 @@ __global__ __launch_bounds__(512) void dec_down_kernel(DecArgs p, int T) {
       staged = t;
     }
     float yacc = 0.0f;
-    for (int i = 0; i < k; ++i) {
-      f32x4_t y[1] = {f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    for (int i = 0; i < kg; ++i) {
+      f32x4_t y[NT];
+      const uint16_t* xpa[NT];
+      const float4* xsa[NT];
+#pragma unroll
+      for (int b = 0; b < NT; ++b) {
+        y[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        xpa[b] = hp + int64_t(NT * i + b) * 2 * I;
+        xsa[b] = hs + int64_t(NT * i + b) * S;
+      }
+      const uint16_t* const (&cxp)[NT] = xpa;
+      const float4* const (&cxs)[NT] = xsa;
       for (int m = 0; m < NS; ++m) {
         issue_next();  // into the slot computed in the previous iteration
         st.wait_oldest();
-        dec_step<BITS, J, 1>(st.slot(st.consumed), y, hp + int64_t(i) * 2 * I,
-                             hs + int64_t(i) * S, I, G, s_lo, s_hi, m, lane, zeros);
+        dec_step<BITS, J, NT, false>(st.slot(st.consumed), y, cxp, cxs, I, G, s_lo, s_hi, m,
+                                     lane, zeros);
         ++st.consumed;
       }
-      yacc = fmaf(s_w[t * k + i], y[0][0] + y[0][1], yacc);
+      // the slots' products are weighted and added in slot order
+#pragma unroll
+      for (int b = 0; b < NT; ++b) yacc = fmaf(s_w[t * k + NT * i + b], y[b][0] + y[b][1], yacc);
     }
     if (g4 == 0) red[wv][c] = yacc;
     lds_barrier();
@@ -727,7 +761,33 @@ __global__ __launch_bounds__(512) void dec_down_kernel(DecArgs p, int T) {
   }
 }
 
+template <int BITS, int J, int NT>
+__global__ __launch_bounds__(512) void dec_down_kernel(DecArgs p, int T) {
+  // The body is compiled for the device only: the host pass (which only
+  // needs the launch stub) rejects its ring-load helper for the two-tile
+  // instances.
+#if defined(__HIP_DEVICE_COMPILE__)
+  extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
+  dec_down_body<BITS, J, NT>(p, T, dsm);
+#endif
+}
+
 namespace {
+
+// dynamic LDS a down kernel may take: 160 KiB less its static tables
+constexpr int kDecDownLdsMax = 160 * 1024 - 2048;
+
+template <int BITS, int J, int NT>
+hipError_t launch_down(const DecArgs& a, int64_t T, unsigned blocks, size_t lds,
+                       hipStream_t stream) {
+  // more than 64 KiB of dynamic LDS must be granted to the kernel explicitly
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dec_down_kernel<BITS, J, NT>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dec_down_kernel<BITS, J, NT>), dim3(blocks), dim3(512), lds, stream, a,
+                     int(T));
+  return hipGetLastError();
+}
 
 template <int BITS, int J>
 hipError_t go_decode(const DecArgs& a, int64_t T, hipStream_t stream) {
@@ -744,13 +804,16 @@ hipError_t go_decode(const DecArgs& a, int64_t T, hipStream_t stream) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t dn_units = T * ((a.H + 15) / 16);
   const unsigned db = unsigned(dn_units < 256 ? dn_units : 256);
-  const size_t dn_lds = size_t(kDecWaves) * DecRing<BITS, J, 1>::BYTES + size_t(a.k) * 4 * a.I +
-                        size_t(a.k) * (a.I / a.group) * 16;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dec_down_kernel<BITS, J>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, int(dn_lds));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((dec_down_kernel<BITS, J>), dim3(db), dim3(512), dn_lds, stream, a, int(T));
-  return hipGetLastError();
+  const size_t parts = size_t(a.k) * 4 * a.I + size_t(a.k) * (a.I / a.group) * 16;
+  // INT4: slot pairs per step when k is even and their ring fits beside the
+  // parts (one token, top-6: 0.5-0.65 us less per layer; INT8 measured
+  // 0.7 us slower with pairs, so it keeps one slot per step)
+  const size_t dn_lds2 = size_t(kDecWaves) * DecRing<BITS, J, 2>::BYTES + parts;
+  if constexpr (BITS == 4)
+    if (a.k % 2 == 0 && dn_lds2 <= size_t(kDecDownLdsMax))
+      return launch_down<BITS, J, 2>(a, T, db, dn_lds2, stream);
+  return launch_down<BITS, J, 1>(a, T, db, size_t(kDecWaves) * DecRing<BITS, J, 1>::BYTES + parts,
+                                 stream);
 }
 
 }  // namespace
