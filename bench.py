@@ -484,6 +484,8 @@ def secondary(dsq, synth, torch, np, dev, cases, x, floor=True):
         torch.cuda.empty_cache()
     if "gemm256" in cases:
         out.append(dense_prefill(dsq, synth, torch, dev))
+    if "gemm256lib" in cases:
+        out.append(dense_prefill_library(synth, torch, dev))
     if "moe256" in cases:
         r, b, g, u, d = build_moe(8, 128, None)
         moe_case("MoE prefill T=256, 256 experts top-6, INT8 g128 SwiGLU, bf16 MFMA",
@@ -567,6 +569,29 @@ def dense_prefill(dsq, synth, torch, dev):
     torch.cuda.empty_cache()
     return rec
 
+
+
+def dense_prefill_library(synth, torch, dev):
+    """Context for the quantized prefill GEMM, not part of the path: the
+    platform's own bf16 GEMM (torch.matmul, i.e. hipBLASLt) on the same shape,
+    M=256, K=N=4096, with plain bf16 weights (twice the bytes of INT8 codes,
+    nothing to dequantize) stored as [N][K] like the packed rows, 32 rotating
+    copies, bf16 output.  Run only when named (--only gemm256lib)."""
+    K = N = 4096
+    Ws = [synth.normal((N, K), 0.02, 0, synth.W, 200 + c, device=dev).to(torch.bfloat16)
+          for c in range(32)]
+    X = synth.normal((256, K), 1.0, 0, synth.X, 5, device=dev).to(torch.bfloat16)
+    Y = torch.empty((256, N), device=dev, dtype=torch.bfloat16)
+    ms = time_calls(lambda i: torch.matmul(X, Ws[i % 32].t(), out=Y), 128, 16, torch)
+    tf = 2 * 256 * N * K / (ms * 1e-3) / 1e12
+    rec = {"workload": "library bf16 GEMM (torch.matmul) M=256 K=N=4096, bf16 weights",
+           "us": round(ms * 1e3, 2), "TFLOP/s": round(tf, 1),
+           "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+           "note": "platform library on unquantized weights, for comparison only"}
+    log(rec)
+    del Ws
+    torch.cuda.empty_cache()
+    return rec
 
 
 def _kernel_name(raw):

@@ -29,9 +29,11 @@
 // registers while the MFMAs of step k run, with one barrier per step.
 //
 // Split-K: the K range is cut into SK slices so that tiles * SK fills the
-// 256 CUs; each slice writes an fp32 partial tile with plain stores.  No
-// fence or counter inside the GEMM: a device-scope fence writes the whole L2
-// back on this chip.  Workgroups are ordered so the two M tiles that share a
+// 256 CUs; each slice writes an fp32 partial tile with device-scope stores,
+// which write through the XCD's L2 as they go (plain stores left 16.8 MB
+// dirty in the L2s at M = 256, K = N = 4096, written back only when the
+// kernel ends: ~1 us more per call).  No fence or counter inside the GEMM: a
+// device-scope fence writes the whole L2 back on this chip.  Workgroups are ordered so the two M tiles that share a
 // W slice run on the same XCD (workgroup b runs on XCD b % 8), and each walks
 // its K steps from a step rotated by its N tile, which spreads the
 // workgroups of an XCD over the L2 channels.
@@ -370,7 +372,8 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs p) {
         }
     return;
   }
-  // split-K: this slice's partial tile, reduced by splitk_reduce_kernel
+  // split-K: this slice's partial tile, reduced by splitk_reduce_kernel;
+  // written through to memory (device scope), read by the next kernel
   float* mine = p.partial + (int64_t(tile) * p.SK + ks) * (kBM * kBN);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -380,7 +383,8 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs p) {
       for (int r = 0; r < 16; ++r) {
         int m, n;
         out_index(i, j, r, m, n);
-        mine[m * kBN + n] = acc[i][j][r];
+        __hip_atomic_store(mine + m * kBN + n, acc[i][j][r], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
 }
 
