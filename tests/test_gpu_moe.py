@@ -63,7 +63,10 @@ SMALL = [(8, 256, 128, 4, 64, 2, 1), (8, 256, 128, 4, 64, 2, 5), (16, 128, 192, 
          (16, 1024, 128, 4, 64, 2, 9), (24, 2048, 128, 8, 128, 3, 40),
          # the largest top_k (32 of 64): decode kernels and the grouped path, and
          # top_k = 16 through the split router
-         (64, 256, 128, 8, 64, 32, 3), (64, 256, 128, 4, 64, 32, 40), (64, 1024, 128, 8, 128, 16, 9)]
+         (64, 256, 128, 8, 64, 32, 3), (64, 256, 128, 4, 64, 32, 40), (64, 1024, 128, 8, 128, 16, 9),
+         # INT4 decode: an odd top_k streams one slot per down step, an even one
+         # two (g64 above, g128 here)
+         (8, 256, 128, 4, 64, 3, 2), (16, 512, 256, 4, 128, 5, 1), (16, 512, 256, 4, 128, 4, 3)]
 
 
 @pytest.mark.parametrize("E,H,I,bits,group,k,T", SMALL)
