@@ -391,7 +391,9 @@ __global__ __launch_bounds__(kThreads) void gemm_mfma_kernel(GemmArgs p) {
 // Y[m][n] = sum over slices q = 0..SK-1 (in that order) of the partial tiles.
 // One thread per 4 consecutive outputs of a row (N % 4 == 0; else one);
 // consecutive threads read consecutive partial floats.  The slices' loads are
-// issued together, 4 at a time, before the adds.
+// issued together, 4 at a time, before the adds.  Each partial is read once:
+// non-temporal loads (0.3 us less per call at M = 256, K = N = 4096; two or
+// four outputs per thread measured slower).
 template <int V>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ partial,
                                                             float* __restrict__ Y, int M, int N,
@@ -404,17 +406,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   const fv* base = reinterpret_cast<const fv*>(partial + int64_t(tile) * SK * (kBM * kBN) +
                                                (m % kBM) * kBN + (n % kBN));
   constexpr int kSlice = kBM * kBN / V;
-  fv v = base[0];
+  auto ld = [&](int q) { return __builtin_nontemporal_load(base + int64_t(q) * kSlice); };
+  fv v = ld(0);
   int q = 1;
   for (; q + 4 <= SK; q += 4) {
-    const fv a = base[int64_t(q) * kSlice], b = base[int64_t(q + 1) * kSlice],
-             c = base[int64_t(q + 2) * kSlice], d = base[int64_t(q + 3) * kSlice];
+    const fv a = ld(q), b = ld(q + 1), c = ld(q + 2), d = ld(q + 3);
     v += a;
     v += b;
     v += c;
     v += d;
   }
-  for (; q < SK; ++q) v += base[int64_t(q) * kSlice];
+  for (; q < SK; ++q) v += ld(q);
   *reinterpret_cast<fv*>(Y + i) = v;
 }
 
