@@ -322,8 +322,8 @@ __device__ __forceinline__ void stage_parts(const float* __restrict__ src, int64
 // once, not once per wave).  The pieces are fetched by direct global->LDS
 // loads: 16-byte chunk j of row r lands at position j ^ swz(r) of the row, so
 // the MFMA operand reads (16 rows at once) fall on distinct banks; the rows'
-// (scale, zp) of the step land beside them.  DEPTH steps are in flight; only
-// this wave reads its ring, so no barrier is needed.
+// (scale, zp) of the step land beside them.  A ring holds DEPTH steps, chosen
+// per kernel; only this wave reads its ring, so no barrier is needed.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int dswz(int r) { return (r >> 1) & 7; }
 
@@ -333,11 +333,9 @@ struct DecRing {
   static constexpr int LB = J * BITS;                 // code bytes per lane, tile and group
   static constexpr int CSLOT = NT * 2048;
   static constexpr int WSLOT = CSLOT + NT * 16 * L * 8;
-  static constexpr int DEPTH = NT == 2 ? DSQ_DEC_GU_DEPTH : DSQ_DEC_DN_DEPTH;  // steps per ring
   static constexpr int PPR = L >= 2 ? L / 2 : 2;      // direct-load pieces per metadata row
   static constexpr int PB = L >= 2 ? 16 : 4;          // bytes per piece
   static constexpr int PER_STEP = 3 * NT;             // direct loads per step
-  static constexpr int BYTES = DEPTH * WSLOT;         // LDS per wave
 };
 
 // Per-lane offsets of a wave's tiles (step 0 of its share).
@@ -471,13 +469,15 @@ __device__ __forceinline__ void dec_step(const uint8_t* slot, f32x4_t (&y)[NT],
 // A wave's ring of streamed steps.  Steps are numbered over the wave's whole
 // sequence (units one after another), so the loads of the next unit are in
 // flight while the current unit is reduced.
-template <int BITS, int J, int NT>
+template <int BITS, int J, int NT, int DEPTH_>
 struct DecStream {
   using R = DecRing<BITS, J, NT>;
+  static constexpr int DEPTH = DEPTH_;                // steps per ring
+  static constexpr int BYTES = DEPTH * R::WSLOT;      // LDS per wave
   uint8_t* ring;
   int issued = 0;     // steps issued
   int consumed = 0;   // steps computed
-  __device__ __forceinline__ uint8_t* slot(int g) const { return ring + (g % R::DEPTH) * R::WSLOT; }
+  __device__ __forceinline__ uint8_t* slot(int g) const { return ring + (g % DEPTH) * R::WSLOT; }
   // Wait for the oldest outstanding step (the one about to be computed).
   __device__ __forceinline__ void wait_oldest() const {
     const int ahead = issued - consumed - 1;  // steps issued after it
@@ -503,6 +503,7 @@ struct DecStream {
 template <int BITS, int J>
 __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
   using R = DecRing<BITS, J, 2>;
+  using St = DecStream<BITS, J, 2, DSQ_DEC_GU_DEPTH>;
   extern __shared__ __attribute__((aligned(16))) uint8_t dsm[];
   __shared__ int s_e[4 * 32];
   __shared__ float s_w[4 * 32];
@@ -515,8 +516,8 @@ __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
   const int c = lane & 15, g4 = lane >> 4;
   const int H = p.H, I = p.I, G = p.group, S = H / G, k = p.k;
   uint8_t* rings = dsm;                                                      // [8][DEPTH][WSLOT]
-  uint16_t* xp = reinterpret_cast<uint16_t*>(dsm + kDecWaves * R::BYTES);    // [2][H]
-  float4* xs = reinterpret_cast<float4*>(dsm + kDecWaves * R::BYTES + 4 * H);  // [S]
+  uint16_t* xp = reinterpret_cast<uint16_t*>(dsm + kDecWaves * St::BYTES);    // [2][H]
+  float4* xs = reinterpret_cast<float4*>(dsm + kDecWaves * St::BYTES + 4 * H);  // [S]
 
   if (threadIdx.x < 4) zeros[threadIdx.x] = 0u;
   // token 0's activation is loaded first and converted once the first weight
@@ -545,8 +546,8 @@ __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
   auto unit_of = [&](int j) { return int(blockIdx.x) + j * int(gridDim.x); };
   if (unit_of(0) >= units) return;
 
-  DecStream<BITS, J, 2> st;
-  st.ring = rings + wv * R::BYTES;
+  St st;
+  st.ring = rings + wv * St::BYTES;
   // lookahead position (unit index j, step m) and its lane offsets
   int lj = 0, lm = 0;
   DecLane<BITS, J, 2> ln;
@@ -568,7 +569,7 @@ __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
       if (unit_of(lj) < units) lane_for(lj);
     }
   };
-  for (int d = 0; d < R::DEPTH - 1; ++d) issue_next();
+  for (int d = 0; d < St::DEPTH - 1; ++d) issue_next();
   stage_store(x0, 1, H, G, xp, xs, threadIdx.x, 512);
   lds_barrier();
 
@@ -641,6 +642,7 @@ __global__ __launch_bounds__(512) void dec_gateup_kernel(DecArgs p, int T) {
 template <int BITS, int J, int NT>
 __device__ __forceinline__ void dec_down_body(const DecArgs& p, int T, uint8_t* dsm) {
   using R = DecRing<BITS, J, NT>;
+  using St = DecStream<BITS, J, NT, DSQ_DEC_DN_DEPTH>;
   __shared__ float red[kDecWaves][16];
   __shared__ __attribute__((aligned(16))) uint32_t zeros[4];
   __shared__ int32_t s_rows[32];
@@ -651,8 +653,8 @@ __device__ __forceinline__ void dec_down_body(const DecArgs& p, int T, uint8_t* 
   const int c = lane & 15, g4 = lane >> 4;
   const int H = p.H, I = p.I, G = p.group, S = I / G, k = p.k;
   uint8_t* rings = dsm;                                                       // [8][DEPTH][WSLOT]
-  uint16_t* hp = reinterpret_cast<uint16_t*>(dsm + kDecWaves * R::BYTES);     // [k][2][I]
-  float4* hs = reinterpret_cast<float4*>(dsm + kDecWaves * R::BYTES + int64_t(k) * 4 * I);
+  uint16_t* hp = reinterpret_cast<uint16_t*>(dsm + kDecWaves * St::BYTES);     // [k][2][I]
+  float4* hs = reinterpret_cast<float4*>(dsm + kDecWaves * St::BYTES + int64_t(k) * 4 * I);
   if (threadIdx.x < 4) zeros[threadIdx.x] = 0u;
   // the first token's activations and the routing are loaded together; the
   // activations are converted once the first weight loads are in flight
@@ -673,8 +675,8 @@ __device__ __forceinline__ void dec_down_body(const DecArgs& p, int T, uint8_t* 
   auto unit_of = [&](int j) { return int(blockIdx.x) + j * int(gridDim.x); };
   if (unit_of(0) >= units) return;
 
-  DecStream<BITS, J, NT> st;
-  st.ring = rings + wv * R::BYTES;
+  St st;
+  st.ring = rings + wv * St::BYTES;
   // lookahead position (unit j, slot group i of NT slots, step m)
   int lj = 0, li = 0, lm = 0;
   const int kg = k / NT;  // slot groups (NT divides k)
@@ -691,7 +693,7 @@ __device__ __forceinline__ void dec_down_body(const DecArgs& p, int T, uint8_t* 
   lane_for(0, 0);
   auto issue_next = [&]() {
     if (unit_of(lj) >= units) return;
-    uint8_t* const sp = st.ring + (st.issued % R::DEPTH) * R::WSLOT;
+    uint8_t* const sp = st.ring + (st.issued % St::DEPTH) * R::WSLOT;
     dec_issue<BITS, J, NT>(ln, sp, lm, lane);
     ++st.issued;
     if (++lm == NS) {
@@ -703,7 +705,7 @@ __device__ __forceinline__ void dec_down_body(const DecArgs& p, int T, uint8_t* 
       if (unit_of(lj) < units) lane_for(lj, li);
     }
   };
-  for (int d = 0; d < R::DEPTH - 1; ++d) issue_next();
+  for (int d = 0; d < St::DEPTH - 1; ++d) issue_next();
   stage_store(h0, k, I, G, hp, hs, threadIdx.x, 512);
   lds_barrier();
 
@@ -793,7 +795,8 @@ template <int BITS, int J>
 hipError_t go_decode(const DecArgs& a, int64_t T, hipStream_t stream) {
   const int64_t gu_units = T * a.k * ((a.I + 15) / 16);
   const unsigned gb = unsigned(gu_units < 256 ? gu_units : 256);
-  const size_t gu_lds = size_t(kDecWaves) * DecRing<BITS, J, 2>::BYTES + size_t(4) * a.H +
+  const size_t gu_lds = size_t(kDecWaves) * DecStream<BITS, J, 2, DSQ_DEC_GU_DEPTH>::BYTES +
+                        size_t(4) * a.H +
                         size_t(a.H / a.group) * 16;
   // more than 64 KiB of dynamic LDS must be granted to the kernel explicitly
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&dec_gateup_kernel<BITS, J>),
@@ -808,12 +811,12 @@ hipError_t go_decode(const DecArgs& a, int64_t T, hipStream_t stream) {
   // INT4: slot pairs per step when k is even and their ring fits beside the
   // parts (one token, top-6: 0.5-0.65 us less per layer; INT8 measured
   // 0.7 us slower with pairs, so it keeps one slot per step)
-  const size_t dn_lds2 = size_t(kDecWaves) * DecRing<BITS, J, 2>::BYTES + parts;
+  const size_t dn_lds2 = size_t(kDecWaves) * DecStream<BITS, J, 2, DSQ_DEC_DN_DEPTH>::BYTES + parts;
   if constexpr (BITS == 4)
     if (a.k % 2 == 0 && dn_lds2 <= size_t(kDecDownLdsMax))
       return launch_down<BITS, J, 2>(a, T, db, dn_lds2, stream);
-  return launch_down<BITS, J, 1>(a, T, db, size_t(kDecWaves) * DecRing<BITS, J, 1>::BYTES + parts,
-                                 stream);
+  return launch_down<BITS, J, 1>(
+      a, T, db, size_t(kDecWaves) * DecStream<BITS, J, 1, DSQ_DEC_DN_DEPTH>::BYTES + parts, stream);
 }
 
 }  // namespace
