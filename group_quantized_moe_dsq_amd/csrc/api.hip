@@ -55,6 +55,13 @@ dsq_status check_qweight(const dsq_qweight* W) {
   return DSQ_OK;
 }
 
+// The matrix-core kernels (grouped GEMM, decode) address one entry's codes
+// and its (scale, zp) table with 32-bit buffer offsets: an entry must stay
+// below 2 GiB there (a larger one would read zeros past 2 GiB, not fault).
+bool entry_fits_32(const dsq_qweight* W) {
+  return layout_of(W->bits, W->group, W->K, W->N).stride <= int64_t(INT32_MAX);
+}
+
 dsq_status hip_status(hipError_t e) {
   if (e == hipSuccess) return DSQ_OK;
   if (e == hipErrorNoDevice || e == hipErrorInvalidDevice) return DSQ_ERR_NO_DEVICE;
@@ -243,6 +250,7 @@ dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float*
   if (!aligned(X, 16) || !aligned(Y, 4)) return DSQ_ERR_ALIGN;
   const bool bf16 = use_bf16(math, M);
   if (W->group == kSuperGroup && (M >= 2 || bf16)) return DSQ_ERR_UNSUPPORTED;  // GEMV only
+  if (M >= 2 && !bf16 && !entry_fits_32(W)) return DSQ_ERR_UNSUPPORTED;
   if (M >= 2 || bf16) {
     const size_t need = dsq_gemm_workspace_bytes(M, W->N, W->K, math);
     if (need == 0) return DSQ_ERR_UNSUPPORTED;
@@ -390,6 +398,7 @@ dsq_status check_moe(const float* X, const float* router_w, const float* bias,
       down->group != gate->group)
     return DSQ_ERR_SHAPE;
   if (gate->group == kSuperGroup) return DSQ_ERR_UNSUPPORTED;  // GEMV only
+  if (!entry_fits_32(gate) || !entry_fits_32(down)) return DSQ_ERR_UNSUPPORTED;
   if (T < 0 || top_k <= 0 || top_k > E64) return DSQ_ERR_SHAPE;
   if (T > 65536 || E64 > 4096 || top_k > 32) return DSQ_ERR_UNSUPPORTED;
   if (!aligned(X, 16) || !aligned(router_w, 16) || !aligned(Y, 16) || (bias && !aligned(bias, 4)))

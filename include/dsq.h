@@ -195,7 +195,9 @@ dsq_status dsq_gemv(const dsq_qweight* W, int64_t expert, const float* x, float*
  * are summed in fp32: |err| <= 1e-2 * sum|x w| per output.
  * A workspace query of 0 for M >= 2 (or for BF16_MFMA) means the shape is
  * beyond the limits (dsq_gemm then returns DSQ_ERR_UNSUPPORTED); BF16_MFMA
- * needs M*K*4 and N*K below 2^31.
+ * needs M*K*4 and N*K below 2^31; FP32 with M >= 2 needs one packed entry
+ * (dsq_packed_bytes(bits, group, K, N, 1)) below 2^31 bytes, else
+ * DSQ_ERR_UNSUPPORTED.
  */
 size_t dsq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t math);
 dsq_status dsq_gemm(const dsq_qweight* W, int64_t expert, const float* X, float* Y, int64_t M,
@@ -314,7 +316,9 @@ dsq_status dsq_gemv_topk(const dsq_qweight* W, int64_t expert, const float* x, f
  *   [E] (tokens routed to each expert; the pages log overloaded experts).
  * Limits: T <= 65536, E <= 4096, 1 <= top_k <= min(E, 32); the activation
  * tiles of the grouped GEMM must stay below 2 GiB (about T * top_k * max(H, I)
- * * 4 bytes for FP32): dsq_moe_workspace_bytes returns 0 beyond that.
+ * * 4 bytes for FP32): dsq_moe_workspace_bytes returns 0 beyond that; one
+ * expert's packed gate (and down) matrix (dsq_packed_bytes(bits, group, K, N,
+ * 1)) must stay below 2^31 bytes, else DSQ_ERR_UNSUPPORTED.
  */
 size_t dsq_moe_workspace_bytes(int64_t T, int32_t E, int32_t top_k, int64_t H, int64_t I,
                                int32_t math);

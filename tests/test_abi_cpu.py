@@ -131,6 +131,30 @@ def test_moe_validation_and_workspace_query():
     assert dsq.moe_workspace_bytes(5, E, 9, H, I, 0) == 0
 
 
+def test_matrix_core_paths_reject_entries_of_2gib():
+    """The grouped GEMM and decode kernels address one expert's codes and
+    (scale, zp) with 32-bit offsets: an entry of 2 GiB or more is refused up
+    front, not computed wrongly."""
+    L = dsq.lib()
+    fake = ctypes.c_void_p(0x40000)
+    # INT8 g64, K = 65536, N = 32768: 2 GiB of codes + 256 MiB of metadata per entry
+    H, I, E = 65536, 32768, 2
+    assert dsq.packed_bytes(8, 64, H, I, 1) > (1 << 31)
+    g, rg = desc(8, 64, H, I, E)
+    u, ru = desc(8, 64, H, I, E)
+    dn, rd = desc(8, 64, I, H, E)
+    assert rg == ru == rd == 0
+    rc = L.dsq_moe_ffn(fake, fake, None, ctypes.byref(g), ctypes.byref(u), ctypes.byref(dn), 1,
+                       2, 0, fake, fake, 1 << 40, None, None, None, None, None)
+    assert rc == -5
+    # the dense FP32 path with M >= 2 runs the same grouped kernel
+    assert L.dsq_gemm(ctypes.byref(g), 0, fake, fake, 2, dsq.MATH_FP32, fake, 1 << 40, None) == -5
+    # just below the limit the shape is accepted up to the device check
+    g2, _ = desc(8, 64, 4096, 4096, 1)
+    assert L.dsq_gemm(ctypes.byref(g2), 0, fake, fake, 2, dsq.MATH_FP32, fake, 1 << 40,
+                      None) != -5
+
+
 def test_superblock_format_shapes_and_limits():
     # group 256 is the 4-bit super-block format: 16-byte block headers
     N, K = 10, 512
