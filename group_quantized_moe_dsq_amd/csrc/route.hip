@@ -6,6 +6,8 @@
 // (hnwysp.cn/news/134870) §3.4 (softmax with the maximum subtracted), §3.5
 // (router = a linear layer, top-k by a greater-first sort of (score, index)
 // pairs, tokens gathered per expert, weighted sum of the expert outputs).
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -523,7 +525,11 @@ __device__ __forceinline__ void group_place(int j, int e, int rank, const int32_
   }
 }
 
-// Few tokens: one workgroup; bitmap [E][ceil(T/32)], built with atomics.
+// Few tokens: one workgroup; bitmap [E][ceil(T/32)], built with atomics, in
+// LDS when it fits beside the tables (LBM; no memory round trips but the
+// routing's load and the outputs' stores), else in the scratch memory.
+constexpr int kGroupLdsWords = 3072;  // E * ceil(T/32): 256 experts x 256 tokens is 2048
+template <bool LBM>
 __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__ idx, int T, int k,
                                                      int E, uint32_t* __restrict__ bm,
                                                      int32_t* __restrict__ counts,
@@ -537,19 +543,24 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__
   __shared__ int32_t s_off[kGroupMaxE + 1];
   __shared__ int32_t s_act[kGroupMaxE + 1];
   __shared__ int32_t s_tile[kGroupMaxE + 1];
+  __shared__ uint32_t s_bm[LBM ? kGroupLdsWords : 1];
+  // a bitmap in memory is built with device-scope atomics: read it past L1
+  typedef typename std::conditional<LBM, uint32_t, volatile uint32_t>::type word_t;
+  word_t* const B = LBM ? s_bm : bm;
   const int W = (T + 31) / 32;
   const int nent = T * k;
-  for (int i = threadIdx.x; i < E * W; i += blockDim.x) bm[i] = 0u;
+  for (int i = threadIdx.x; i < E * W; i += blockDim.x) B[i] = 0u;
   __syncthreads();
   for (int j = threadIdx.x; j < nent; j += blockDim.x) {
     const int e = idx[j];
     const int t = j / k;
-    if (unsigned(e) < unsigned(E)) atomicOr(&bm[e * W + (t >> 5)], 1u << (t & 31));
+    if (unsigned(e) < unsigned(E))
+      atomicOr(const_cast<uint32_t*>(&B[e * W + (t >> 5)]), 1u << (t & 31));
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x) {
     int c = 0;
-    const volatile uint32_t* row = bm + e * W;
+    const word_t* row = B + e * W;
     for (int w = 0; w < W; ++w) c += __popc(row[w]);
     s_off[e] = c;
   }
@@ -564,8 +575,7 @@ __global__ __launch_bounds__(1024) void group_kernel(const int32_t* __restrict__
       continue;
     }
     const int t = j / k;
-    // the bitmap was built with device-scope atomics: read it past L1
-    const volatile uint32_t* row = bm + e * W;
+    const word_t* row = B + e * W;
     int rank = 0;
     for (int w = 0; w < (t >> 5); ++w) rank += __popc(row[w]);
     rank += __popc(row[t >> 5] & ((1u << (t & 31)) - 1u));
@@ -667,8 +677,14 @@ hipError_t launch_group(const int32_t* idx, int64_t T, int32_t k, int32_t E, uin
   if (tiles && tpt <= 0) return hipErrorInvalidValue;
   if (E <= 0 || E > kGroupMaxE || T < 0) return hipErrorInvalidValue;
   if (T <= kGroupSmallT) {
-    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(1024), 0, stream, idx, int(T), k, E, scratch,
-                       counts, offsets, perm, pos, active, n_active, tpt, tiles, n_tiles);
+    if (int64_t(E) * ((T + 31) / 32) <= kGroupLdsWords)
+      hipLaunchKernelGGL(group_kernel<true>, dim3(1), dim3(1024), 0, stream, idx, int(T), k, E,
+                         scratch, counts, offsets, perm, pos, active, n_active, tpt, tiles,
+                         n_tiles);
+    else
+      hipLaunchKernelGGL(group_kernel<false>, dim3(1), dim3(1024), 0, stream, idx, int(T), k, E,
+                         scratch, counts, offsets, perm, pos, active, n_active, tpt, tiles,
+                         n_tiles);
     return hipGetLastError();
   }
   const int W = int((T + 31) / 32);
