@@ -29,7 +29,9 @@ def test_gemm_fp32_within_bound(bits, group, M, N, K):
 
 
 BF16_CASES = [(8, 128, 1, 64, 256), (8, 128, 16, 128, 1024), (4, 64, 33, 100, 320),
-              (8, 64, 64, 257, 512), (4, 128, 100, 64, 4096), (8, 128, 256, 512, 4096)]
+              (8, 64, 64, 257, 512), (4, 128, 100, 64, 4096), (8, 128, 256, 512, 4096),
+              # three and five 128-row tiles of M, the last ragged (and a ragged N tile)
+              (4, 64, 300, 640, 2048), (8, 64, 513, 200, 768)]
 
 
 @pytest.mark.parametrize("bits,group,M,N,K", BF16_CASES)
