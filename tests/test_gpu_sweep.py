@@ -3,8 +3,10 @@ the other GPU tests.  Every case draws its sizes from a fixed generator (the
 case number is its seed; the sizes are printed before it runs) and checks the
 library against the oracle with the bounds those tests use: the fp32 paths
 within 1e-5 * sum|x w| per output, the bf16 matrix-core paths within
-1e-2 * sum|x w| plus a normwise relative error of at most 1e-2, and the MoE
-layer through the same routing, weight and output checks as test_gpu_moe."""
+1e-2 * sum|x w| plus a normwise relative error of at most 1e-2, the MoE
+layer through the same routing, weight and output checks as test_gpu_moe,
+the super-block GEMV as test_gpu_sb4 does, and the top-k selection bitwise
+(indices and value bits) as test_gpu_head does."""
 import numpy as np
 import pytest
 
@@ -92,3 +94,30 @@ def test_sweep_moe(case):
     fx = MoeFixture(E, H, I, bits, group, seed=14 + case, bias_std=bias or None)
     X = synth.normal((T, H), 1.0, 14, synth.X, case, device="cuda")
     check_moe(fx, X, k, math, 1e-5 if math == dsq.MATH_FP32 else 1e-2)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_sweep_superblock_gemv(case):
+    from test_gpu_sb4 import gemv_check
+    r = rng(5, case)
+    N = int(r.integers(1, 2500))
+    K = 256 * int(r.integers(1, 49))  # up to 12288: the long-row kernel too
+    say(f"sweep sb4 gemv case={case} N={N} K={K}")
+    gemv_check(N, K, 900 + case)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_sweep_topk(case):
+    import torch
+
+    from test_gpu_head import bits, values
+    r = rng(6, case)
+    N = int(r.integers(1, 200000))
+    k = int(r.integers(1, min(N, 256) + 1))
+    pattern = str(r.choice(["normal", "ties", "special"]))
+    say(f"sweep topk case={case} N={N} k={k} pattern={pattern}")
+    y = values(N, pattern, 1000 + case)
+    idx, val = dsq.topk(torch.from_numpy(y).cuda(), k)
+    ref_idx, ref_val = oracle.topk(y, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_array_equal(bits(val.cpu().numpy()), bits(ref_val))
