@@ -26,8 +26,11 @@
  *     allocates nothing, keeps no state between calls (the expert cache keeps
  *     its state in caller-owned tables) and never synchronises (except
  *     dsq_moe_ffn_cached, whose host must see the routing); every call only
- *     enqueues work on `stream` (a hipStream_t, NULL = the default stream).  Calls are re-entrant; two calls that share a
- *     workspace must be ordered on one stream.
+ *     enqueues kernels on `stream` (a hipStream_t, NULL = the default
+ *     stream): no memset, copy or synchronisation, so a call can be captured
+ *     into a HIP graph and replayed (dsq_moe_ffn_cached excepted).  Calls are
+ *     re-entrant; two calls that share a workspace must be ordered on one
+ *     stream.
  *   - Arguments are validated on the host before anything is enqueued.  A
  *     failed check returns a negative dsq_status and enqueues nothing, so no
  *     output is written.  Launch failures return DSQ_ERR_HIP.
