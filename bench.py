@@ -477,7 +477,7 @@ def secondary(dsq, synth, torch, np, dev, cases, x, floor=True):
         if "moe32" in cases:
             bias = synth.normal((256,), 1.0, 0, synth.BIAS, 0, device=dev)
             moe_case("MoE batched decode T=32 skewed (router bias ~N(0,1)), INT4 g64",
-                     dsq.MoeLayer(r, g, u, d, bias, N_EXPERT_USED), 32, 8, dsq.MATH_FP32, 4, 64, 16,
+                     dsq.MoeLayer(r, g, u, d, bias, N_EXPERT_USED), 32, 8, dsq.MATH_FP32, 4, 64, 64,
                      case="moe32", kernels=("dsq::gmm_kernel<4, 2, 2, true>",
                                             "dsq::gmm_kernel<4, 2, 2, false>"))
         del g, u, d
@@ -489,7 +489,7 @@ def secondary(dsq, synth, torch, np, dev, cases, x, floor=True):
     if "moe256" in cases:
         r, b, g, u, d = build_moe(8, 128, None)
         moe_case("MoE prefill T=256, 256 experts top-6, INT8 g128 SwiGLU, bf16 MFMA",
-                 dsq.MoeLayer(r, g, u, d, None, N_EXPERT_USED), 256, 1, dsq.MATH_BF16_MFMA, 8, 128, 8,
+                 dsq.MoeLayer(r, g, u, d, None, N_EXPERT_USED), 256, 1, dsq.MATH_BF16_MFMA, 8, 128, 24,
                  case="moe256", kernels=("dsq::gmm_kernel<8, 4, 1, true>",
                                          "dsq::gmm_kernel<8, 4, 1, false>"))
         del g, u, d
