@@ -309,7 +309,7 @@ def main():
             hval = torch.empty(k, device=dev)
             hws = torch.empty(dsq.topk_workspace_bytes(NV, k) + 256, dtype=torch.uint8, device=dev)
             hms = time_calls(lambda i: dsq.gemv_topk(WV, x, k, y=yv, idx=hidx, values=hval,
-                                                     workspace=hws), 20, 2, torch)
+                                                     workspace=hws), 100, 2, torch)
             gbs = bytesv / (hms * 1e-3) / 1e9
             head.append({"workload": f"output head: INT8 g64 vocab GEMV 4096x129280 + top-{k} "
                                      "of the logits", "us": round(hms * 1e3, 2),
