@@ -761,10 +761,6 @@ def cpu_baseline_child(reps):
     import oracle
     from group_quantized_moe_dsq_amd import synth
 
-    # importing torch (through synth) resets the OpenMP thread count of the
-    # process; the parent's OMP_NUM_THREADS is applied again here
-    if os.environ.get("OMP_NUM_THREADS"):
-        oracle.set_threads(int(os.environ["OMP_NUM_THREADS"]))
     K, NV = N_EMBD, N_VOCAB
     # the same shapes, seeds and distributions as the GPU phase, drawn with
     # the CPU generator
@@ -781,6 +777,11 @@ def cpu_baseline_child(reps):
         oracle.qmatmul_f32(x, m4)
         oracle.qmatmul_f32(x, mv)
 
+    # torch (the input generator) sets the process's OpenMP thread count
+    # when it starts its own pool, from its environment: the parent's count
+    # is applied here, after the last torch call and before the timed passes
+    if os.environ.get("OMP_NUM_THREADS"):
+        oracle.set_threads(int(os.environ["OMP_NUM_THREADS"]))
     step()
     times = []
     for _ in range(reps):
@@ -799,8 +800,8 @@ def cpu_baseline(reps):
     import subprocess
 
     topo = cpu_topology()
-    env = dict(os.environ, OMP_NUM_THREADS=str(topo["threads"]), OMP_PROC_BIND="close",
-               OMP_PLACES="cores")
+    env = dict(os.environ, OMP_NUM_THREADS=str(topo["threads"]),
+               MKL_NUM_THREADS=str(topo["threads"]), OMP_PROC_BIND="close", OMP_PLACES="cores")
     r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-child",
                         "--cpu-reps", str(reps)], env=env, capture_output=True, text=True,
                        timeout=900)
