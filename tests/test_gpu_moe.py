@@ -66,7 +66,9 @@ SMALL = [(8, 256, 128, 4, 64, 2, 1), (8, 256, 128, 4, 64, 2, 5), (16, 128, 192, 
          (64, 256, 128, 8, 64, 32, 3), (64, 256, 128, 4, 64, 32, 40), (64, 1024, 128, 8, 128, 16, 9),
          # INT4 decode: an odd top_k streams one slot per down step, an even one
          # two (g64 above, g128 here)
-         (8, 256, 128, 4, 64, 3, 2), (16, 512, 256, 4, 128, 5, 1), (16, 512, 256, 4, 128, 4, 3)]
+         (8, 256, 128, 4, 64, 3, 2), (16, 512, 256, 4, 128, 5, 1), (16, 512, 256, 4, 128, 4, 3),
+         # 256 tokens per expert: 32 token tiles of 8 in every expert
+         (16, 256, 128, 4, 64, 4, 1024)]
 
 
 @pytest.mark.parametrize("E,H,I,bits,group,k,T", SMALL)
@@ -80,7 +82,9 @@ def test_moe_fp32_small(E, H, I, bits, group, k, T):
 @pytest.mark.parametrize("E,H,I,bits,group,k,T", [(8, 256, 128, 8, 128, 2, 64),
                                                   (16, 512, 256, 4, 64, 4, 100),
                                                   (8, 128, 192, 8, 64, 3, 7),
-                                                  (16, 1024, 256, 4, 64, 4, 100)])
+                                                  (16, 1024, 256, 4, 64, 4, 100),
+                                                  # ~770 tokens per expert: 49 token tiles
+                                                  (16, 512, 256, 8, 128, 6, 2048)])
 def test_moe_bf16_small(E, H, I, bits, group, k, T):
     say(f"moe bf16 E={E} H={H} I={I} bits={bits} group={group} k={k} T={T}")
     fx = MoeFixture(E, H, I, bits, group, seed=5)
